@@ -1,0 +1,470 @@
+// extern "C" entry points: argument validation, workspace layout, dispatch.
+// No entry point allocates, frees or synchronises; all scratch lives in the
+// caller's workspace and all work goes on the caller's stream.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "common.hpp"
+
+namespace {
+
+thread_local char g_err[512];
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+#define CHECK(cond, code, ...) \
+  do {                         \
+    if (!(cond)) return fail(code, __VA_ARGS__); \
+  } while (0)
+
+#define HIPCHECK(expr)                                                   \
+  do {                                                                   \
+    hipError_t e_ = (expr);                                              \
+    if (e_ != hipSuccess)                                                \
+      return fail(SPARSE_EHIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int64_t esize(int dt) { return dt == SPARSE_F32 ? 4 : (dt == SPARSE_BF16 ? 2 : 1); }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// ------------------------------------------------------------------ layout
+struct IndexLayout {
+  int rows_per_b = 1;  // R
+  int rows = 0;        // B * R
+  int n_units = 0;
+  int n_chunks = 0;
+  size_t scores = 0, hist = 0, cand_key = 0, cand_idx = 0, chunk_cnt = 0,
+         depth = 0, plane_w = 0, score_c = 0, end = 0;
+};
+
+IndexLayout index_layout(const sparse_index_args& a, bool with_scores) {
+  IndexLayout L;
+  L.rows_per_b = a.kind == SPARSE_SCORE_BITPLANE ? a.n_kv_heads : 1;
+  L.rows = a.batch * L.rows_per_b;
+  const int bs = a.kind == SPARSE_SCORE_DOT ? a.block_size : 1;
+  L.n_units = (int)ceil_div(a.n, bs);
+  L.n_chunks = (int)ceil_div(L.n_units, sd::kTopkChunk);
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
+  const size_t cells = (size_t)L.rows * L.n_units;
+  L.scores = with_scores ? take(cells * 4) : 0;
+  L.hist = take((size_t)L.rows * sd::kHistBins * 4);
+  L.cand_key = take(cells * 4);
+  L.cand_idx = take(cells * 4);
+  L.chunk_cnt = take((size_t)L.rows * std::max(L.n_chunks, 1) * 4);
+  if (a.kind == SPARSE_SCORE_BITPLANE) {
+    const size_t hd = (size_t)a.batch * a.n_kv_heads * a.head_dim;
+    L.depth = take(hd);
+    L.plane_w = take(hd * 4 * 4);
+    L.score_c = take((size_t)a.batch * a.n_kv_heads * 4);
+  }
+  L.end = off;
+  return L;
+}
+
+// Fixed split heuristic (no runtime tuning): enough workgroups to cover
+// the 256 compute units about twice, but never fewer than 64 tokens per
+// split.
+int attn_splits(const sparse_attn_args& a, int k_tokens) {
+  if (k_tokens <= 0) return 1;
+  int groups;
+  int min_tok;
+  if (a.dtype == SPARSE_F32) {
+    groups = a.n_q_heads;
+    min_tok = 64;
+  } else if (a.d_qk == 576) {
+    groups = a.n_q_heads / 32;
+    min_tok = 256;
+  } else {
+    groups = a.n_kv_heads;
+    min_tok = 64;
+  }
+  const int64_t base = (int64_t)std::max(a.batch, 1) * std::max(groups, 1);
+  int s = (int)ceil_div(512, base);
+  s = std::min<int64_t>(s, std::max<int64_t>(1, k_tokens / min_tok));
+  s = std::max(s, 1);
+  if (a.dtype == SPARSE_F32) s = std::max<int>(s, (int)ceil_div(k_tokens, 2048));
+  return s;
+}
+
+struct AttnLayout {
+  int k_tokens = 0, splits = 1;
+  size_t part = 0, staging = 0, end = 0;
+};
+
+AttnLayout attn_layout(const sparse_attn_args& a, int k_tokens, size_t base) {
+  AttnLayout L;
+  L.k_tokens = k_tokens;
+  L.splits = attn_splits(a, k_tokens);
+  size_t off = base;
+  auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
+  if (L.splits > 1)
+    L.part = take((size_t)a.batch * a.n_q_heads * L.splits * (a.d_v + 2) * 4);
+  if (a.hot_slot) L.staging = take((size_t)a.batch * k_tokens * a.d_qk * 2);
+  L.end = off;
+  return L;
+}
+
+// -------------------------------------------------------------- validation
+int check_index(const sparse_index_args* a) {
+  CHECK(a, SPARSE_EINVAL, "index args is NULL");
+  CHECK(a->batch >= 0 && a->n >= 0, SPARSE_EINVAL, "negative batch or n");
+  CHECK(a->kind >= 0 && a->kind <= 2, SPARSE_EINVAL, "unknown score kind %d", a->kind);
+  CHECK(a->head_dim == 128, SPARSE_EUNSUPPORTED, "head_dim %d (only 128)", a->head_dim);
+  CHECK(a->n <= (1 << 22) * 1, SPARSE_EUNSUPPORTED, "n %d above 4194304", a->n);
+  if (a->batch == 0 || a->n == 0) return SPARSE_OK;
+  CHECK(a->q && aligned16(a->q), SPARSE_EINVAL, "q NULL or not 16-byte aligned");
+  CHECK(a->n_heads >= 1, SPARSE_EINVAL, "n_heads %d", a->n_heads);
+  const int64_t qe = esize(a->q_dtype);
+  CHECK((a->q_stride_h * qe) % 16 == 0 && (a->q_stride_b * qe) % 16 == 0,
+        SPARSE_EINVAL, "q strides must be multiples of 16 bytes");
+  CHECK(a->q_stride_h >= a->head_dim, SPARSE_EINVAL, "q_stride_h < head_dim");
+  if (a->kind == SPARSE_SCORE_DOT) {
+    CHECK(a->q_dtype == SPARSE_F32 || a->q_dtype == SPARSE_BF16, SPARSE_EUNSUPPORTED,
+          "DOT q dtype");
+    CHECK(a->k_dtype == a->q_dtype, SPARSE_EUNSUPPORTED, "DOT needs q and keys of one dtype");
+    CHECK(a->block_size == 1 || a->block_size == 64, SPARSE_EUNSUPPORTED,
+          "block_size %d (1 or 64)", a->block_size);
+  } else {
+    CHECK(a->block_size == 1, SPARSE_EUNSUPPORTED, "block_size must be 1 for this kind");
+    CHECK(a->q_dtype == SPARSE_BF16, SPARSE_EUNSUPPORTED, "q must be bf16 for this kind");
+  }
+  if (a->kind != SPARSE_SCORE_BITPLANE) {
+    CHECK(a->keys && aligned16(a->keys), SPARSE_EINVAL, "keys NULL or not 16-byte aligned");
+    const int64_t ke = esize(a->k_dtype);
+    CHECK((a->k_stride_t * ke) % 16 == 0 && (a->k_stride_b * ke) % 16 == 0,
+          SPARSE_EINVAL, "key strides must be multiples of 16 bytes");
+    CHECK(a->k_stride_t >= a->head_dim, SPARSE_EINVAL, "k_stride_t < head_dim");
+  }
+  if (a->kind == SPARSE_SCORE_LIGHTNING) {
+    CHECK(a->k_dtype == SPARSE_E4M3FN, SPARSE_EUNSUPPORTED, "LIGHTNING keys must be e4m3fn");
+    CHECK(a->n_heads == 32 || a->n_heads == 64, SPARSE_EUNSUPPORTED,
+          "LIGHTNING n_heads %d (32 or 64)", a->n_heads);
+    CHECK(a->head_w && a->k_scale, SPARSE_EINVAL, "head_w / k_scale NULL");
+  }
+  if (a->kind == SPARSE_SCORE_BITPLANE) {
+    CHECK(a->n_kv_heads >= 1 && a->n_heads % a->n_kv_heads == 0, SPARSE_EINVAL,
+          "n_heads %d not a multiple of n_kv_heads %d", a->n_heads, a->n_kv_heads);
+    CHECK(a->planes && a->chan_zero && a->chan_scale && a->chan_var, SPARSE_EINVAL,
+          "planes / chan_zero / chan_scale / chan_var NULL");
+    CHECK(a->bit_budget >= 0 && a->bit_budget <= 4 * a->head_dim, SPARSE_EINVAL,
+          "bit_budget %d outside 0..%d", a->bit_budget, 4 * a->head_dim);
+  }
+  return SPARSE_OK;
+}
+
+int check_attn(const sparse_attn_args* a, int sel_heads, int k, int sel_unit) {
+  CHECK(a, SPARSE_EINVAL, "attn args is NULL");
+  CHECK(a->batch >= 0 && a->n >= 0, SPARSE_EINVAL, "negative batch or n");
+  CHECK(k >= 1, SPARSE_EINVAL, "k %d < 1", k);
+  CHECK(sel_unit == 1 || sel_unit == 64, SPARSE_EUNSUPPORTED, "sel_unit %d", sel_unit);
+  CHECK(a->n_q_heads >= 1 && a->n_kv_heads >= 1 && a->n_q_heads % a->n_kv_heads == 0,
+        SPARSE_EINVAL, "heads %d / %d", a->n_q_heads, a->n_kv_heads);
+  CHECK(sel_heads == 1 || sel_heads == a->n_kv_heads, SPARSE_EINVAL,
+        "sel_heads %d must be 1 or n_kv_heads", sel_heads);
+  const int G = a->n_q_heads / a->n_kv_heads;
+  if (a->dtype == SPARSE_F32) {
+    CHECK(a->d_qk == 128 && a->d_v == 128, SPARSE_EUNSUPPORTED, "f32 attention needs 128/128");
+    CHECK(a->hot_slot == nullptr, SPARSE_EUNSUPPORTED, "hot buffer needs bf16 latent rows");
+  } else if (a->dtype == SPARSE_BF16) {
+    const bool mla = a->d_qk == 576 && a->d_v == 512 && a->v_cache == nullptr &&
+                     a->n_kv_heads == 1 && a->n_q_heads % 32 == 0;
+    const bool gqa = a->d_qk == 128 && a->d_v == 128 && a->v_cache != nullptr && G <= 16;
+    CHECK(mla || gqa, SPARSE_EUNSUPPORTED,
+          "bf16 attention shapes: latent 576/512 (1 KV head, Hq %% 32 == 0) or "
+          "128/128 with <= 16 query heads per KV head");
+  } else {
+    return fail(SPARSE_EUNSUPPORTED, "attention dtype %d", a->dtype);
+  }
+  if (a->batch == 0) return SPARSE_OK;
+  CHECK(a->q && aligned16(a->q), SPARSE_EINVAL, "q NULL or not 16-byte aligned");
+  const int64_t e = esize(a->dtype);
+  CHECK((a->q_stride_h * e) % 16 == 0 && (a->q_stride_b * e) % 16 == 0, SPARSE_EINVAL,
+        "q strides must be multiples of 16 bytes");
+  if (a->hot_slot) {
+    CHECK(a->v_cache == nullptr && a->page_table == nullptr, SPARSE_EUNSUPPORTED,
+          "hot buffer: latent contiguous rows only");
+    CHECK(sel_heads == 1, SPARSE_EUNSUPPORTED, "hot buffer: one selection per request");
+    CHECK(a->hot_kv && aligned16(a->hot_kv) && a->host_kv && aligned16(a->host_kv),
+          SPARSE_EINVAL, "hot_kv / host_kv NULL or misaligned");
+    CHECK((a->hot_stride_s * 2) % 16 == 0 && (a->hot_stride_b * 2) % 16 == 0 &&
+              (a->host_stride_t * 2) % 16 == 0 && (a->host_stride_b * 2) % 16 == 0,
+          SPARSE_EINVAL, "hot/host strides must be multiples of 16 bytes");
+  } else {
+    CHECK(a->k_cache && aligned16(a->k_cache), SPARSE_EINVAL,
+          "k_cache NULL or not 16-byte aligned");
+    CHECK(a->v_cache == nullptr || aligned16(a->v_cache), SPARSE_EINVAL,
+          "v_cache not 16-byte aligned");
+    CHECK((a->kv_stride_t * e) % 16 == 0 && (a->kv_stride_h * e) % 16 == 0 &&
+              (a->kv_stride_b * e) % 16 == 0,
+          SPARSE_EINVAL, "KV strides must be multiples of 16 bytes");
+    if (a->page_table) CHECK(a->page_size >= 1, SPARSE_EINVAL, "page_size < 1");
+  }
+  return SPARSE_OK;
+}
+
+sd::TopkPlan make_topk_plan(const IndexLayout& L, char* ws, const float* scores,
+                            int64_t row_stride, const int32_t* valid, int rows_per_valid,
+                            int unit_div, int k, int32_t* idx_out, float* val_out) {
+  sd::TopkPlan p;
+  p.rows = L.rows;
+  p.n_units = L.n_units;
+  p.k = k;
+  p.n_chunks = L.n_chunks;
+  p.rows_per_valid = rows_per_valid;
+  p.row_stride = row_stride;
+  p.scores = scores;
+  p.valid = valid;
+  p.unit_div = unit_div;
+  p.hist = (uint32_t*)(ws + L.hist);
+  p.cand_key = (uint32_t*)(ws + L.cand_key);
+  p.cand_idx = (int32_t*)(ws + L.cand_idx);
+  p.chunk_cnt = (uint32_t*)(ws + L.chunk_cnt);
+  p.idx_out = idx_out;
+  p.val_out = val_out;
+  return p;
+}
+
+int run_topk(const sd::TopkPlan& p, bool hist_ready, hipStream_t s) {
+  if (p.rows == 0) return SPARSE_OK;
+  if (p.n_units == 0) {
+    // nothing valid: the select kernel only pads
+    HIPCHECK(sd::launch_topk_select(p, s));
+    return SPARSE_OK;
+  }
+  if (!hist_ready) {
+    HIPCHECK(sd::launch_zero_u32(p.hist, (int64_t)p.rows * sd::kHistBins, s));
+    HIPCHECK(sd::launch_topk_hist(p, s));
+  }
+  HIPCHECK(sd::launch_topk_filter(p, s));
+  HIPCHECK(sd::launch_topk_select(p, s));
+  return SPARSE_OK;
+}
+
+int run_scores(const sparse_index_args& a, const IndexLayout& L, char* ws, float* scores,
+               uint32_t* hist, hipStream_t s) {
+  sd::ScorePlan sp;
+  sp.a = &a;
+  sp.scores = scores;
+  sp.hist = hist;
+  sp.n_units = L.n_units;
+  sp.depth = nullptr;
+  sp.plane_w = nullptr;
+  sp.score_c = nullptr;
+  switch (a.kind) {
+    case SPARSE_SCORE_DOT:
+      HIPCHECK(sd::launch_score_dot(sp, s));
+      break;
+    case SPARSE_SCORE_LIGHTNING:
+      HIPCHECK(sd::launch_score_lightning(sp, s));
+      break;
+    case SPARSE_SCORE_BITPLANE:
+      sp.depth = (int8_t*)(ws + L.depth);
+      sp.plane_w = (float*)(ws + L.plane_w);
+      sp.score_c = (float*)(ws + L.score_c);
+      HIPCHECK(sd::launch_read_depth(&a, sp.depth, sp.plane_w, sp.score_c, s));
+      HIPCHECK(sd::launch_score_bitplane(sp, s));
+      break;
+  }
+  return SPARSE_OK;
+}
+
+int run_attn(const sparse_attn_args& a, const int32_t* sel, int sel_heads, int k,
+             int sel_unit, float* out, float* lse, char* ws, size_t base, hipStream_t s) {
+  const int k_tokens = k * sel_unit;
+  AttnLayout L = attn_layout(a, k_tokens, base);
+  sd::AttnPlan p;
+  p.a = a;
+  p.sel = sel;
+  p.sel_heads = sel_heads;
+  p.k = k;
+  p.sel_unit = sel_unit;
+  p.out = out;
+  p.lse = lse;
+  p.splits = L.splits;
+  p.part = L.splits > 1 ? (float*)(ws + L.part) : nullptr;
+  p.staging = a.hot_slot ? (uint16_t*)(ws + L.staging) : nullptr;
+  p.k_tokens = k_tokens;
+  if (a.hot_slot) HIPCHECK(sd::launch_miss_fetch(p, s));
+  if (a.dtype == SPARSE_F32) HIPCHECK(sd::launch_attn_f32(p, s));
+  else HIPCHECK(sd::launch_attn_bf16(p, s));
+  if (L.splits > 1) HIPCHECK(sd::launch_attn_combine(p, s));
+  return SPARSE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sparse_abi_version(void) { return SPARSE_ABI_VERSION; }
+
+const char* sparse_strerror(int status) {
+  switch (status) {
+    case SPARSE_OK: return "ok";
+    case SPARSE_EINVAL: return "invalid argument";
+    case SPARSE_EUNSUPPORTED: return "unsupported shape or dtype";
+    case SPARSE_EWORKSPACE: return "workspace too small";
+    case SPARSE_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* sparse_last_error(void) { return g_err; }
+
+int sparse_workspace_size(const sparse_index_args* ia, const sparse_attn_args* aa,
+                          int32_t k, size_t* bytes) {
+  CHECK(bytes, SPARSE_EINVAL, "bytes is NULL");
+  CHECK(ia || aa, SPARSE_EINVAL, "both args NULL");
+  size_t total = 0;
+  int unit = 1;
+  if (ia) {
+    int rc = check_index(ia);
+    if (rc) return rc;
+    total = index_layout(*ia, aa != nullptr).end;
+    unit = ia->kind == SPARSE_SCORE_DOT ? ia->block_size : 1;
+  }
+  if (aa) {
+    CHECK(k >= 1, SPARSE_EINVAL, "k %d < 1", k);
+    total = attn_layout(*aa, k * unit, total).end;
+  }
+  *bytes = total;
+  return SPARSE_OK;
+}
+
+int sparse_topk_workspace_size(int32_t rows, int32_t n_units, int32_t k, size_t* bytes) {
+  CHECK(bytes, SPARSE_EINVAL, "bytes is NULL");
+  CHECK(rows >= 0 && n_units >= 0 && k >= 1, SPARSE_EINVAL, "rows/n_units/k");
+  sparse_index_args a;
+  memset(&a, 0, sizeof(a));
+  a.kind = SPARSE_SCORE_DOT;
+  a.batch = rows;
+  a.n = n_units;
+  a.block_size = 1;
+  *bytes = index_layout(a, false).end;
+  return SPARSE_OK;
+}
+
+int sparse_read_depth(const sparse_index_args* ia, int8_t* depth_out, void* stream) {
+  int rc = check_index(ia);
+  if (rc) return rc;
+  CHECK(ia->kind == SPARSE_SCORE_BITPLANE, SPARSE_EINVAL, "read depth needs kind BITPLANE");
+  if (ia->batch == 0) return SPARSE_OK;
+  CHECK(depth_out, SPARSE_EINVAL, "depth_out NULL");
+  CHECK(ia->q, SPARSE_EINVAL, "q NULL");
+  // the scan weights are a by-product the kernel skips when given NULL
+  hipStream_t s = (hipStream_t)stream;
+  HIPCHECK(sd::launch_read_depth(ia, depth_out, nullptr, nullptr, s));
+  return SPARSE_OK;
+}
+
+int sparse_index_score(const sparse_index_args* ia, float* scores, void* ws,
+                       size_t ws_bytes, void* stream) {
+  int rc = check_index(ia);
+  if (rc) return rc;
+  if (ia->batch == 0 || ia->n == 0) return SPARSE_OK;
+  CHECK(scores, SPARSE_EINVAL, "scores NULL");
+  IndexLayout L = index_layout(*ia, false);
+  if (ia->kind == SPARSE_SCORE_BITPLANE) {
+    CHECK(ws && ws_bytes >= L.end, SPARSE_EWORKSPACE, "workspace %zu < %zu", ws_bytes, L.end);
+  }
+  return run_scores(*ia, L, (char*)ws, scores, nullptr, (hipStream_t)stream);
+}
+
+int sparse_topk(const float* scores, int32_t rows, int32_t n_units, int64_t row_stride,
+                const int32_t* valid_units, int32_t rows_per_valid, int32_t k,
+                int32_t* idx_out, float* val_out, void* ws, size_t ws_bytes, void* stream) {
+  CHECK(rows >= 0 && n_units >= 0, SPARSE_EINVAL, "negative rows or n_units");
+  CHECK(k >= 1 && k <= (1 << 20), SPARSE_EINVAL, "k %d outside 1..1048576", k);
+  CHECK(n_units <= sd::kTopkChunk * 1024, SPARSE_EUNSUPPORTED, "n_units above 4194304");
+  if (rows == 0) return SPARSE_OK;
+  CHECK(idx_out, SPARSE_EINVAL, "idx_out NULL");
+  CHECK(n_units == 0 || scores, SPARSE_EINVAL, "scores NULL");
+  CHECK(row_stride >= n_units, SPARSE_EINVAL, "row_stride < n_units");
+  CHECK(!valid_units || rows_per_valid >= 1, SPARSE_EINVAL, "rows_per_valid < 1");
+  size_t need = 0;
+  sparse_topk_workspace_size(rows, n_units, k, &need);
+  CHECK(ws && ws_bytes >= need, SPARSE_EWORKSPACE, "workspace %zu < %zu", ws_bytes, need);
+  sparse_index_args a;
+  memset(&a, 0, sizeof(a));
+  a.kind = SPARSE_SCORE_DOT;
+  a.batch = rows;
+  a.n = n_units;
+  a.block_size = 1;
+  IndexLayout L = index_layout(a, false);
+  sd::TopkPlan p = make_topk_plan(L, (char*)ws, scores, row_stride, valid_units,
+                                  valid_units ? rows_per_valid : 1, 1, k, idx_out, val_out);
+  return run_topk(p, false, (hipStream_t)stream);
+}
+
+int sparse_gather_attn_decode(const sparse_attn_args* aa, const int32_t* sel,
+                              int32_t sel_heads, int32_t k, int32_t sel_unit, float* out,
+                              float* lse, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_attn(aa, sel_heads, k, sel_unit);
+  if (rc) return rc;
+  if (aa->batch == 0) return SPARSE_OK;
+  CHECK(sel && out, SPARSE_EINVAL, "sel / out NULL");
+  AttnLayout L = attn_layout(*aa, k * sel_unit, 0);
+  CHECK(L.end == 0 || (ws && ws_bytes >= L.end), SPARSE_EWORKSPACE, "workspace %zu < %zu",
+        ws_bytes, L.end);
+  return run_attn(*aa, sel, sel_heads, k, sel_unit, out, lse, (char*)ws, 0,
+                  (hipStream_t)stream);
+}
+
+int sparse_decode_step(const sparse_index_args* ia, const sparse_attn_args* aa, int32_t k,
+                       int32_t* topk_out, float* out, float* lse, void* ws,
+                       size_t ws_bytes, void* stream) {
+  int rc = check_index(ia);
+  if (rc) return rc;
+  const bool bitplane = ia->kind == SPARSE_SCORE_BITPLANE;
+  const int sel_heads = bitplane ? ia->n_kv_heads : 1;
+  const int unit = ia->kind == SPARSE_SCORE_DOT ? ia->block_size : 1;
+  rc = check_attn(aa, sel_heads, k, unit);
+  if (rc) return rc;
+  CHECK(ia->batch == aa->batch, SPARSE_EINVAL, "index batch %d != attention batch %d",
+        ia->batch, aa->batch);
+  CHECK(ia->n <= aa->n, SPARSE_EINVAL, "index n %d > attention n %d", ia->n, aa->n);
+  if (bitplane)
+    CHECK(ia->n_kv_heads == aa->n_kv_heads, SPARSE_EINVAL, "KV heads differ");
+  if (ia->batch == 0) return SPARSE_OK;
+  CHECK(topk_out && out, SPARSE_EINVAL, "topk_out / out NULL");
+  size_t need = 0;
+  rc = sparse_workspace_size(ia, aa, k, &need);
+  if (rc) return rc;
+  CHECK(ws && ws_bytes >= need, SPARSE_EWORKSPACE, "workspace %zu < %zu", ws_bytes, need);
+  hipStream_t s = (hipStream_t)stream;
+  char* w = (char*)ws;
+  IndexLayout L = index_layout(*ia, true);
+  float* scores = (float*)(w + L.scores);
+  sd::TopkPlan tp = make_topk_plan(L, w, scores, L.n_units, ia->seq_lens, L.rows_per_b,
+                                   unit, k, topk_out, nullptr);
+  if (ia->n > 0) {
+    HIPCHECK(sd::launch_zero_u32(tp.hist, (int64_t)tp.rows * sd::kHistBins, s));
+    rc = run_scores(*ia, L, w, scores, tp.hist, s);
+    if (rc) return rc;
+  }
+  rc = run_topk(tp, true, s);
+  if (rc) return rc;
+  return run_attn(*aa, topk_out, sel_heads, k, unit, out, lse, w, L.end, s);
+}
+
+int sparse_host_device_pointer(void* host_ptr, void** dev_ptr) {
+  CHECK(host_ptr && dev_ptr, SPARSE_EINVAL, "NULL pointer");
+  HIPCHECK(hipHostGetDevicePointer(dev_ptr, host_ptr, 0));
+  return SPARSE_OK;
+}
+
+}  // extern "C"

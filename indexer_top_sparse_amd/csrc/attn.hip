@@ -1,0 +1,530 @@
+// Sparse decode attention over the selected KV rows (steps a4, a5, a6).
+//
+// "XM-Sparse" blog, opening paragraph: each decode step attends over only
+// the selected KV entries.  out_h = sum_i softmax_i(scale * q_h . k_i) v_i
+// over the selected rows i, lse_h = log sum_i exp(scale * q_h . k_i).
+//
+// bf16 path (MFMA): a workgroup owns (request, head group, token split) and
+// walks the split's selected tokens in tiles of 32.  Each tile is gathered
+// row by row (page table / hot buffer / staging) into LDS with 16-byte
+// loads, prefetched into registers one tile ahead.  S = q K^T runs on
+// v_mfma_f32_16x16x32_bf16 with q held in registers; an online softmax
+// keeps per-head running max and sum; P V runs on the same MFMA with V read
+// from LDS as 8-token column strips re-packed in registers.  Splits write
+// unnormalised partials that a combine kernel merges by log-sum-exp.
+#include "common.hpp"
+
+namespace sd {
+
+struct RowAddr {
+  // Resolves token t of request b (KV head h) to its K and V row pointers.
+  const sparse_attn_args& a;
+  __device__ __forceinline__ const char* k_row(int b, int h, int t, int64_t stage_row,
+                                               const uint16_t* staging, int esize) const {
+    if (a.hot_slot) {
+      int slot = a.hot_slot[(int64_t)b * a.hs_stride_b + t];
+      if (slot >= 0)
+        return (const char*)a.hot_kv +
+               ((int64_t)b * a.hot_stride_b + (int64_t)slot * a.hot_stride_s) * esize;
+      return (const char*)(staging + stage_row * a.d_qk);
+    }
+    int64_t off;
+    if (a.page_table) {
+      int pg = a.page_table[(int64_t)b * a.pt_stride_b + t / a.page_size];
+      off = ((int64_t)pg * a.page_size + t % a.page_size) * a.kv_stride_t;
+    } else {
+      off = (int64_t)b * a.kv_stride_b + (int64_t)t * a.kv_stride_t;
+    }
+    off += (int64_t)h * a.kv_stride_h;
+    return (const char*)a.k_cache + off * esize;
+  }
+  __device__ __forceinline__ const char* v_row(int b, int h, int t, int esize) const {
+    int64_t off;
+    if (a.page_table) {
+      int pg = a.page_table[(int64_t)b * a.pt_stride_b + t / a.page_size];
+      off = ((int64_t)pg * a.page_size + t % a.page_size) * a.kv_stride_t;
+    } else {
+      off = (int64_t)b * a.kv_stride_b + (int64_t)t * a.kv_stride_t;
+    }
+    off += (int64_t)h * a.kv_stride_h;
+    return (const char*)a.v_cache + off * esize;
+  }
+};
+
+__device__ __forceinline__ int valid_tokens(const sparse_attn_args& a, int b) {
+  if (!a.seq_lens) return a.n;
+  int v = a.seq_lens[b];
+  return v < 0 ? 0 : (v > a.n ? a.n : v);
+}
+
+// Token of selection list position j (-1 if padding or past seq_len).
+__device__ __forceinline__ int sel_token(const int32_t* selrow, int j, int unit,
+                                         int valid) {
+  int u = selrow[j / unit];
+  if (u < 0) return -1;
+  int t = u * unit + (j % unit);
+  return t < valid ? t : -1;
+}
+
+// =================================================================== fp32
+// One workgroup per (request, query head, split); d <= 256.
+constexpr int kF32Threads = 256;
+constexpr int kF32MaxTok = 2048;
+
+__global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(AttnPlan p) {
+  __shared__ float logit_s[kF32MaxTok];
+  __shared__ int tok_s[kF32MaxTok];
+  __shared__ float red_s[kF32Threads / 64];
+  const int split = blockIdx.x;
+  const int hq = blockIdx.y;
+  const int b = blockIdx.z;
+  const sparse_attn_args& A = p.a;
+  const int G = A.n_q_heads / A.n_kv_heads;
+  const int kvh = hq / G;
+  const int selrow_i = p.sel_heads == 1 ? 0 : kvh;
+  const int32_t* selrow = p.sel + ((int64_t)b * p.sel_heads + selrow_i) * p.k;
+  const int valid = valid_tokens(A, b);
+  const int tps = (p.k_tokens + p.splits - 1) / p.splits;
+  const int j0 = split * tps;
+  const int j1 = min(j0 + tps, p.k_tokens);
+  const int cnt = max(0, j1 - j0);
+  const float* q = (const float*)A.q + (int64_t)b * A.q_stride_b + (int64_t)hq * A.q_stride_h;
+  const int tid = threadIdx.x;
+  RowAddr ra{A};
+  float lmax = -__builtin_huge_valf();
+  for (int i = tid; i < cnt; i += kF32Threads) {
+    int t = sel_token(selrow, j0 + i, p.sel_unit, valid);
+    tok_s[i] = t;
+    float lg = -__builtin_huge_valf();
+    if (t >= 0) {
+      const float* kr = (const float*)ra.k_row(b, kvh, t, 0, nullptr, 4);
+      float acc = 0.f;
+      for (int d = 0; d < A.d_qk; ++d) acc = fmaf(q[d], kr[d], acc);
+      lg = acc * A.sm_scale;
+    }
+    logit_s[i] = lg;
+    lmax = fmaxf(lmax, lg);
+  }
+  for (int off = 32; off >= 1; off >>= 1) lmax = fmaxf(lmax, __shfl_xor(lmax, off, 64));
+  if ((tid & 63) == 0) red_s[tid >> 6] = lmax;
+  __syncthreads();
+  float m = red_s[0];
+  for (int w = 1; w < kF32Threads / 64; ++w) m = fmaxf(m, red_s[w]);
+  __syncthreads();
+  float lsum = 0.f;
+  for (int i = tid; i < cnt; i += kF32Threads) {
+    float e = (m == -__builtin_huge_valf()) ? 0.f : __expf(logit_s[i] - m);
+    logit_s[i] = e;
+    lsum += e;
+  }
+  for (int off = 32; off >= 1; off >>= 1) lsum += __shfl_xor(lsum, off, 64);
+  if ((tid & 63) == 0) red_s[tid >> 6] = lsum;
+  __syncthreads();
+  float l = 0.f;
+  for (int w = 0; w < kF32Threads / 64; ++w) l += red_s[w];
+  for (int d = tid; d < A.d_v; d += kF32Threads) {
+    float acc = 0.f;
+    for (int i = 0; i < cnt; ++i) {
+      int t = tok_s[i];
+      if (t < 0) continue;
+      const float* vr = A.v_cache
+          ? (const float*)ra.v_row(b, kvh, t, 4)
+          : (const float*)ra.k_row(b, kvh, t, 0, nullptr, 4);
+      acc = fmaf(logit_s[i], vr[d], acc);
+    }
+    const int64_t oh = (int64_t)b * A.n_q_heads + hq;
+    if (p.splits == 1) {
+      p.out[oh * A.d_v + d] = l > 0.f ? acc / l : 0.f;
+    } else {
+      p.part[(oh * p.splits + split) * (A.d_v + 2) + d] = acc;
+    }
+  }
+  if (tid == 0) {
+    const int64_t oh = (int64_t)b * A.n_q_heads + hq;
+    if (p.splits == 1) {
+      if (p.lse) p.lse[oh] = l > 0.f ? m + __logf(l) : -__builtin_huge_valf();
+    } else {
+      float* pp = p.part + (oh * p.splits + split) * (A.d_v + 2);
+      pp[A.d_v] = m;
+      pp[A.d_v + 1] = l;
+    }
+  }
+}
+
+hipError_t launch_attn_f32(const AttnPlan& p, hipStream_t s) {
+  dim3 grid(p.splits, p.a.n_q_heads, p.a.batch);
+  attn_f32_kernel<<<grid, kF32Threads, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+// =================================================================== bf16
+constexpr int kAttnThreads = 256;
+constexpr int kTT = 32;  // tokens per tile
+
+template <int DQK, int DV, int HG, bool LATENT>
+struct AttnCfg {
+  static constexpr int kRowK = DQK + 8;                 // LDS row stride (elements)
+  static constexpr int kRowV = LATENT ? kRowK : DV + 8;
+  static constexpr int kCprK = DQK * 2 / 16;            // 16-byte chunks per K row
+  static constexpr int kCprV = LATENT ? 0 : DV * 2 / 16;
+  static constexpr int kChunks = kTT * (kCprK + kCprV);
+  static constexpr int kNch = (kChunks + kAttnThreads - 1) / kAttnThreads;
+  static constexpr int kKSteps = DQK / 32;              // QK k-steps
+  static constexpr int kMT = HG / 16;                   // head m-tiles
+  static constexpr int kNTQ = kTT / 16;                 // QK token n-tiles
+  static constexpr int kWC = DV / 4;                    // PV columns per wave
+  static constexpr int kCPL = kWC / 16;                 // PV columns per lane
+  static constexpr int kTPR = kAttnThreads / HG;        // softmax threads per row
+  static constexpr int kEPT = kTT / kTPR;               // softmax entries per thread
+  static_assert(kMT * kNTQ <= 4, "QK tiles exceed the waves");
+  static_assert(kCPL == 2 || kCPL == 4 || kCPL == 8, "PV strip width");
+};
+
+template <int DQK, int DV, int HG, bool LATENT>
+__global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(AttnPlan p) {
+  using C = AttnCfg<DQK, DV, HG, LATENT>;
+  __shared__ __attribute__((aligned(16))) uint16_t ks_s[kTT * C::kRowK];
+  __shared__ __attribute__((aligned(16))) uint16_t vs_s[LATENT ? 8 : kTT * C::kRowV];
+  __shared__ float s_s[HG * kTT];
+  __shared__ __attribute__((aligned(16))) uint16_t p_s[HG * (kTT + 8)];
+  __shared__ float alpha_s[HG];
+  __shared__ float m_s[HG];
+  __shared__ float l_s[HG];
+  __shared__ int tok_s[kTT];
+
+  const sparse_attn_args& A = p.a;
+  const int split = blockIdx.x;
+  const int grp = blockIdx.y;
+  const int b = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wid = tid >> 6;
+  const int G = A.n_q_heads / A.n_kv_heads;
+  // head group: MLA-style (one KV head, HG heads per group) or one KV head
+  // per group with its G <= HG query heads (rows past G are padding)
+  const int kvh = (A.n_kv_heads == 1) ? 0 : grp;
+  const int head0 = (A.n_kv_heads == 1) ? grp * HG : grp * G;
+  const int greal = (A.n_kv_heads == 1) ? HG : G;
+  const int selrow_i = p.sel_heads == 1 ? 0 : kvh;
+  const int32_t* selrow = p.sel + ((int64_t)b * p.sel_heads + selrow_i) * p.k;
+  const int valid = valid_tokens(A, b);
+  const int tps = (p.k_tokens + p.splits - 1) / p.splits;
+  const int j0 = split * tps;
+  const int j1 = min(j0 + tps, p.k_tokens);
+  const int ntiles = j1 > j0 ? (j1 - j0 + kTT - 1) / kTT : 0;
+  const int64_t stage_base = ((int64_t)b * p.sel_heads + selrow_i) * p.k_tokens;
+  RowAddr ra{A};
+
+  // ---- q operands (A of QK): head 16*mt + (lane%16), dims 32s + 8(lane/16)
+  const int qmt = wid / C::kNTQ;
+  const int qnt = wid % C::kNTQ;
+  const bool qk_wave = qmt < C::kMT;
+  bf16x8 qa[C::kKSteps];
+  {
+    const int hr = (qk_wave ? qmt : 0) * 16 + (lane & 15);
+    const bool real = qk_wave && hr < greal;
+    const uint16_t* qp = (const uint16_t*)A.q + (int64_t)b * A.q_stride_b +
+                         (int64_t)(head0 + (real ? hr : 0)) * A.q_stride_h + 8 * (lane >> 4);
+#pragma unroll
+    for (int s = 0; s < C::kKSteps; ++s) {
+      if (real) qa[s] = *(const bf16x8*)(qp + 32 * s);
+      else for (int e = 0; e < 8; ++e) qa[s][e] = (__bf16)0.f;
+    }
+  }
+
+  // ---- tile gather (registers), one tile ahead
+  uint4 pre[C::kNch];
+  auto gather = [&](int tile) {
+    const int jt = j0 + tile * kTT;
+#pragma unroll
+    for (int i = 0; i < C::kNch; ++i) {
+      const int q = tid + i * kAttnThreads;
+      pre[i] = make_uint4(0u, 0u, 0u, 0u);
+      if (q < C::kChunks) {
+        const bool isv = q >= kTT * C::kCprK;
+        const int qq = isv ? q - kTT * C::kCprK : q;
+        const int cpr = isv ? C::kCprV : C::kCprK;
+        const int row = qq / cpr;
+        const int cc = qq % cpr;
+        const int j = jt + row;
+        int t = (j < j1) ? sel_token(selrow, j, p.sel_unit, valid) : -1;
+        if (t >= 0) {
+          const char* base = isv ? ra.v_row(b, kvh, t, 2)
+                                 : ra.k_row(b, kvh, t, stage_base + j, p.staging, 2);
+          pre[i] = *(const uint4*)(base + 16 * cc);
+        }
+      }
+    }
+  };
+  auto commit = [&](int tile) {
+#pragma unroll
+    for (int i = 0; i < C::kNch; ++i) {
+      const int q = tid + i * kAttnThreads;
+      if (q < C::kChunks) {
+        const bool isv = q >= kTT * C::kCprK;
+        const int qq = isv ? q - kTT * C::kCprK : q;
+        const int cpr = isv ? C::kCprV : C::kCprK;
+        const int row = qq / cpr;
+        const int cc = qq % cpr;
+        uint16_t* dst = isv ? vs_s + row * C::kRowV : ks_s + row * C::kRowK;
+        *(uint4*)(dst + 8 * cc) = pre[i];
+      }
+    }
+    if (tid < kTT) {
+      const int j = j0 + tile * kTT + tid;
+      tok_s[tid] = (j < j1) ? sel_token(selrow, j, p.sel_unit, valid) : -1;
+    }
+  };
+
+  // ---- softmax row state (replicated across the kTPR threads of a row)
+  const int srow = tid / C::kTPR;
+  const int ssub = tid % C::kTPR;
+  float m_run = -__builtin_huge_valf();
+  float l_run = 0.f;
+
+  // ---- output accumulators: rows 16*mt + 4*(lane/16) + i, columns
+  // wid*kWC + kCPL*(lane%16) + nt
+  f32x4 o[C::kMT][C::kCPL];
+#pragma unroll
+  for (int mt = 0; mt < C::kMT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < C::kCPL; ++nt)
+      for (int e = 0; e < 4; ++e) o[mt][nt][e] = 0.f;
+
+  if (ntiles > 0) gather(0);
+  for (int tile = 0; tile < ntiles; ++tile) {
+    __syncthreads();  // previous tile fully consumed
+    commit(tile);
+    __syncthreads();
+    if (tile + 1 < ntiles) gather(tile + 1);
+
+    // ---- S = scale * q K^T  (wave: 16 heads x 16 tokens)
+    if (qk_wave) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      const uint16_t* kr = ks_s + (16 * qnt + (lane & 15)) * C::kRowK + 8 * (lane >> 4);
+#pragma unroll
+      for (int s = 0; s < C::kKSteps; ++s) {
+        bf16x8 kv = *(const bf16x8*)(kr + 32 * s);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], kv, acc, 0, 0, 0);
+      }
+      const int col = 16 * qnt + (lane & 15);
+      const bool ok = tok_s[col] >= 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * qmt + 4 * (lane >> 4) + i;
+        s_s[r * kTT + col] = ok ? acc[i] * A.sm_scale : -__builtin_huge_valf();
+      }
+    }
+    __syncthreads();
+
+    // ---- online softmax over the tile
+    {
+      float sv[C::kEPT];
+      float tmax = -__builtin_huge_valf();
+#pragma unroll
+      for (int e = 0; e < C::kEPT; ++e) {
+        sv[e] = s_s[srow * kTT + ssub * C::kEPT + e];
+        tmax = fmaxf(tmax, sv[e]);
+      }
+#pragma unroll
+      for (int off = C::kTPR / 2; off >= 1; off >>= 1)
+        tmax = fmaxf(tmax, __shfl_xor(tmax, off, 64));
+      const float m_new = fmaxf(m_run, tmax);
+      const bool none = (m_new == -__builtin_huge_valf());
+      const float alpha = none ? 1.f : __expf(m_run - m_new);
+      float psum = 0.f;
+#pragma unroll
+      for (int e = 0; e < C::kEPT; ++e) {
+        float pe = none ? 0.f : __expf(sv[e] - m_new);
+        __bf16 pb = (__bf16)pe;
+        psum += (float)pb;
+        p_s[srow * (kTT + 8) + ssub * C::kEPT + e] = __builtin_bit_cast(uint16_t, pb);
+      }
+#pragma unroll
+      for (int off = C::kTPR / 2; off >= 1; off >>= 1) psum += __shfl_xor(psum, off, 64);
+      l_run = alpha * l_run + psum;
+      m_run = m_new;
+      if (ssub == 0) alpha_s[srow] = alpha;
+    }
+    __syncthreads();
+
+    // ---- O = alpha * O + P V  (wave: all heads x kWC columns)
+    {
+      float al[C::kMT][4];
+#pragma unroll
+      for (int mt = 0; mt < C::kMT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) al[mt][i] = alpha_s[16 * mt + 4 * (lane >> 4) + i];
+#pragma unroll
+      for (int mt = 0; mt < C::kMT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < C::kCPL; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[mt][nt][i] *= al[mt][i];
+
+      bf16x8 pa[C::kMT];
+#pragma unroll
+      for (int mt = 0; mt < C::kMT; ++mt)
+        pa[mt] = *(const bf16x8*)(p_s + (16 * mt + (lane & 15)) * (kTT + 8) + 8 * (lane >> 4));
+
+      // V strip: tokens 8*(lane/16) + i, columns wid*kWC + kCPL*(lane%16) ..
+      const uint16_t* vbase = (LATENT ? ks_s : vs_s) + (8 * (lane >> 4)) * C::kRowV +
+                              wid * C::kWC + C::kCPL * (lane & 15);
+      constexpr int DW = C::kCPL / 2;  // dwords per token strip
+      uint32_t raw[8][DW];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint16_t* vp = vbase + i * C::kRowV;
+        if constexpr (DW == 4) {
+          uint4 v = *(const uint4*)vp;
+          raw[i][0] = v.x; raw[i][1] = v.y; raw[i][2] = v.z; raw[i][3] = v.w;
+        } else if constexpr (DW == 2) {
+          uint2 v = *(const uint2*)vp;
+          raw[i][0] = v.x; raw[i][1] = v.y;
+        } else {
+          raw[i][0] = *(const uint32_t*)vp;
+        }
+      }
+#pragma unroll
+      for (int nt = 0; nt < C::kCPL; ++nt) {
+        const uint32_t sel = (nt & 1) ? 0x07060302u : 0x05040100u;
+        uint32_t d[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          d[e] = __builtin_amdgcn_perm(raw[2 * e + 1][nt >> 1], raw[2 * e][nt >> 1], sel);
+        bf16x8 vb = __builtin_bit_cast(bf16x8, make_uint4(d[0], d[1], d[2], d[3]));
+#pragma unroll
+        for (int mt = 0; mt < C::kMT; ++mt)
+          o[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[mt], vb, o[mt][nt], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- epilogue
+  if (ssub == 0) {
+    m_s[srow] = m_run;
+    l_s[srow] = l_run;
+  }
+  __syncthreads();
+  const int Hq = A.n_q_heads;
+#pragma unroll
+  for (int mt = 0; mt < C::kMT; ++mt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * mt + 4 * (lane >> 4) + i;
+      if (r >= greal) continue;
+      const int64_t oh = (int64_t)b * Hq + head0 + r;
+      const float l = l_s[r];
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+      for (int nt = 0; nt < C::kCPL; ++nt) {
+        const int col = wid * C::kWC + C::kCPL * (lane & 15) + nt;
+        if (p.splits == 1) p.out[oh * DV + col] = o[mt][nt][i] * inv;
+        else p.part[(oh * p.splits + split) * (DV + 2) + col] = o[mt][nt][i];
+      }
+    }
+  }
+  if (tid < greal && tid < HG) {
+    const int64_t oh = (int64_t)b * Hq + head0 + tid;
+    const float m = m_s[tid], l = l_s[tid];
+    if (p.splits == 1) {
+      if (p.lse) p.lse[oh] = l > 0.f ? m + __logf(l) : -__builtin_huge_valf();
+    } else {
+      float* pp = p.part + (oh * p.splits + split) * (DV + 2);
+      pp[DV] = m;
+      pp[DV + 1] = l;
+    }
+  }
+}
+
+hipError_t launch_attn_bf16(const AttnPlan& p, hipStream_t s) {
+  const sparse_attn_args& a = p.a;
+  if (a.d_qk == 576 && a.d_v == 512 && a.v_cache == nullptr && a.n_kv_heads == 1) {
+    dim3 grid(p.splits, a.n_q_heads / 32, a.batch);
+    attn_bf16_kernel<576, 512, 32, true><<<grid, kAttnThreads, 0, s>>>(p);
+  } else if (a.d_qk == 128 && a.d_v == 128 && a.v_cache != nullptr) {
+    dim3 grid(p.splits, a.n_kv_heads, a.batch);
+    attn_bf16_kernel<128, 128, 16, false><<<grid, kAttnThreads, 0, s>>>(p);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// ================================================================ combine
+// Merge split partials of one (request, head): M = max m_s,
+// L = sum l_s exp(m_s - M), out = sum o_s exp(m_s - M) / L, lse = M + log L.
+__global__ __launch_bounds__(256) void attn_combine_kernel(AttnPlan p) {
+  const int hq = blockIdx.x;
+  const int b = blockIdx.y;
+  const sparse_attn_args& A = p.a;
+  const int dv = A.d_v;
+  const int S = p.splits;
+  const int64_t oh = (int64_t)b * A.n_q_heads + hq;
+  const float* pp = p.part + oh * S * (dv + 2);
+  float M = -__builtin_huge_valf();
+  for (int s = 0; s < S; ++s) M = fmaxf(M, pp[s * (dv + 2) + dv]);
+  float L = 0.f;
+  for (int s = 0; s < S; ++s) {
+    float m = pp[s * (dv + 2) + dv];
+    float l = pp[s * (dv + 2) + dv + 1];
+    if (l > 0.f) L += l * __expf(m - M);
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  for (int d = threadIdx.x; d < dv; d += blockDim.x) {
+    float acc = 0.f;
+    for (int s = 0; s < S; ++s) {
+      float m = pp[s * (dv + 2) + dv];
+      float l = pp[s * (dv + 2) + dv + 1];
+      if (l > 0.f) acc += pp[s * (dv + 2) + d] * __expf(m - M);
+    }
+    p.out[oh * dv + d] = acc * inv;
+  }
+  if (threadIdx.x == 0 && p.lse)
+    p.lse[oh] = L > 0.f ? M + __logf(L) : -__builtin_huge_valf();
+}
+
+hipError_t launch_attn_combine(const AttnPlan& p, hipStream_t s) {
+  dim3 grid(p.a.n_q_heads, p.a.batch);
+  attn_combine_kernel<<<grid, 256, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+// ============================================================ miss fetch
+// "XM-Sparse" blog, Figure 1 caption and KV-lifecycle list: selected
+// entries that are not in the HBM hot buffer are fetched from host memory.
+// One thread per 16-byte chunk of a missed row: reads the row through the
+// device-visible alias of the pinned host buffer (PCIe) and writes it to the
+// workspace staging slot of its selection position.
+__global__ __launch_bounds__(256) void miss_fetch_kernel(AttnPlan p) {
+  const sparse_attn_args& A = p.a;
+  const int b = blockIdx.y;
+  const int cpr = A.d_qk * 2 / 16;
+  const int valid = valid_tokens(A, b);
+  const int32_t* selrow = p.sel + (int64_t)b * p.sel_heads * p.k;
+  const int64_t total = (int64_t)p.k_tokens * cpr;
+  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < total;
+       q += (int64_t)gridDim.x * blockDim.x) {
+    const int j = (int)(q / cpr);
+    const int cc = (int)(q % cpr);
+    const int t = sel_token(selrow, j, p.sel_unit, valid);
+    if (t < 0) continue;
+    if (A.hot_slot[(int64_t)b * A.hs_stride_b + t] >= 0) continue;
+    const char* src = (const char*)A.host_kv +
+                      ((int64_t)b * A.host_stride_b + (int64_t)t * A.host_stride_t) * 2;
+    uint16_t* dst = p.staging + ((int64_t)b * p.k_tokens + j) * A.d_qk;
+    *(uint4*)((char*)dst + 16 * cc) = *(const uint4*)(src + 16 * cc);
+  }
+}
+
+hipError_t launch_miss_fetch(const AttnPlan& p, hipStream_t s) {
+  const int cpr = p.a.d_qk * 2 / 16;
+  int64_t per_b = (int64_t)p.k_tokens * cpr;
+  int gx = (int)((per_b + 255) / 256);
+  if (gx > 64) gx = 64;
+  dim3 grid(gx, p.a.batch);
+  miss_fetch_kernel<<<grid, 256, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+}  // namespace sd

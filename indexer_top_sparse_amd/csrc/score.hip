@@ -1,0 +1,483 @@
+// Index scores (step a2) and Fathom read depth (step a1).
+//
+// Every kernel here streams the HBM-resident index once, keeps the query in
+// registers, writes fp32 unit scores and, when asked, adds each valid unit's
+// top-12-bit key to a per-row 4096-bin histogram (the first radix digit of
+// the top-k select) so the select never re-reads the scores for it.
+#include "common.hpp"
+
+namespace sd {
+
+// Per-workgroup histogram in LDS, flushed to the row's global histogram.
+struct LdsHist {
+  uint32_t* h;
+  __device__ void clear(int nt) {
+    for (int i = threadIdx.x; i < kHistBins; i += nt) h[i] = 0u;
+  }
+  __device__ void add(float s) { atomicAdd(&h[score_key(s) >> 20], 1u); }
+  __device__ void flush(uint32_t* g, int nt) {
+    for (int i = threadIdx.x; i < kHistBins; i += nt)
+      if (h[i]) atomicAdd(&g[i], h[i]);
+  }
+};
+
+__device__ __forceinline__ int valid_len(const int32_t* seq_lens, int b,
+                                         int n) {
+  if (!seq_lens) return n;
+  int v = seq_lens[b];
+  return v < 0 ? 0 : (v > n ? n : v);
+}
+
+// ========================================================================
+// DOT: s_t = sum_h q_h . k_t  (= q_bar . k_t, q_bar = sum_h q_h formed once
+// in fp64 and rounded to fp32), optional max over 64-token blocks.
+//
+// Layout: LPR = 16 lanes cover one 256-byte bf16 row (32 lanes for fp32);
+// a wave loads RPI = 64/LPR rows per instruction, fully coalesced.  Each
+// lane keeps partial dots of LPR rows and a reduce-scatter butterfly over
+// the LPR lanes leaves one finished token score per lane.
+// ========================================================================
+template <typename T>
+struct DotTraits;
+template <>
+struct DotTraits<float> {
+  static constexpr int kLPR = 32;  // 128 fp32 = 512 B = 32 x 16 B
+  static constexpr int kPerLoad = 4;
+};
+template <>
+struct DotTraits<uint16_t> {
+  static constexpr int kLPR = 16;  // 128 bf16 = 256 B = 16 x 16 B
+  static constexpr int kPerLoad = 8;
+};
+
+__device__ __forceinline__ void load_elems(const float* p, float* x) {
+  f32x4 v = *(const f32x4*)p;
+  x[0] = v[0]; x[1] = v[1]; x[2] = v[2]; x[3] = v[3];
+}
+__device__ __forceinline__ void load_elems(const uint16_t* p, float* x) {
+  uint4 v = *(const uint4*)p;
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = __uint_as_float(w[i] << 16);
+    x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+
+constexpr int kDotThreads = 256;
+constexpr int kDotTokensPerWG = 2048;
+
+template <typename T, int BLOCK>
+__global__ __launch_bounds__(kDotThreads) void score_dot_kernel(
+    sparse_index_args a, float* __restrict__ scores, uint32_t* hist,
+    int n_units) {
+  constexpr int LPR = DotTraits<T>::kLPR;
+  constexpr int PL = DotTraits<T>::kPerLoad;
+  constexpr int RPI = kWave / LPR;        // rows per load instruction
+  constexpr int BATCH = LPR * RPI;        // = 64 tokens per wave batch
+  __shared__ float qbar_s[128];
+  __shared__ uint32_t hist_s[kHistBins];
+  LdsHist lh{hist_s};
+
+  const int b = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
+  const int n = a.n;
+  const int valid = valid_len(a.seq_lens, b, n);
+
+  if (hist) lh.clear(kDotThreads);
+  if (threadIdx.x < 128) {
+    double acc = 0.0;
+    for (int h = 0; h < a.n_heads; ++h) {
+      const T* qh = (const T*)a.q + (int64_t)b * a.q_stride_b +
+                    (int64_t)h * a.q_stride_h;
+      float x;
+      if constexpr (sizeof(T) == 4) x = qh[threadIdx.x];
+      else x = bf16_bits_to_f32(qh[threadIdx.x]);
+      acc += (double)x;
+    }
+    qbar_s[threadIdx.x] = (float)acc;
+  }
+  __syncthreads();
+
+  const int j = lane % LPR;   // 16-byte chunk of the row this lane reads
+  const int g = lane / LPR;   // row within a load instruction
+  float qv[PL];
+#pragma unroll
+  for (int e = 0; e < PL; ++e) qv[e] = qbar_s[j * PL + e];
+
+  const T* kb = (const T*)a.keys + (int64_t)b * a.k_stride_b;
+  const int t_begin = blockIdx.x * kDotTokensPerWG;
+  const int t_end = min(t_begin + kDotTokensPerWG, n);
+  float* srow = scores + (int64_t)b * n_units;
+
+  for (int base = t_begin + wid * BATCH; base < t_end;
+       base += BATCH * (kDotThreads / kWave)) {
+    float part[LPR];
+#pragma unroll
+    for (int i = 0; i < LPR; ++i) {
+      int t = base + i * RPI + g;
+      int tc = t < n ? t : n - 1;
+      float x[PL];
+      load_elems(kb + (int64_t)tc * a.k_stride_t + j * PL, x);
+      float acc = 0.f;
+#pragma unroll
+      for (int e = 0; e < PL; ++e) acc = fmaf(qv[e], x[e], acc);
+      part[i] = acc;
+    }
+    // reduce-scatter over the LPR lanes of a row group
+#pragma unroll
+    for (int m = LPR / 2; m >= 1; m >>= 1) {
+#pragma unroll
+      for (int i = 0; i < m; ++i) {
+        // lanes with (j & m) keep the upper half [i + m], others the lower
+        float send = (j & m) ? part[i] : part[i + m];
+        float keep = (j & m) ? part[i + m] : part[i];
+        float recv = __shfl_xor(send, m, 64);
+        part[i] = keep + recv;
+      }
+    }
+    // lane holds token base + j*RPI + g
+    const int t = base + j * RPI + g;
+    float s = part[0];
+    if (t >= valid) s = -__builtin_huge_valf();
+    if constexpr (BLOCK == 1) {
+      if (t < n) {
+        srow[t] = s;
+        if (hist && t < valid) lh.add(s);
+      }
+    } else {
+      // BATCH == BLOCK == 64: one block per wave batch
+      float m = s;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+      const int u = base / BLOCK;
+      if (lane == 0 && u < n_units) {
+        srow[u] = m;
+        if (hist && base < valid) lh.add(m);
+      }
+    }
+  }
+  if (hist) {
+    __syncthreads();
+    lh.flush(hist + (int64_t)b * kHistBins, kDotThreads);
+  }
+}
+
+hipError_t launch_score_dot(const ScorePlan& p, hipStream_t s) {
+  const sparse_index_args& a = *p.a;
+  dim3 grid((a.n + kDotTokensPerWG - 1) / kDotTokensPerWG, a.batch);
+  if (a.k_dtype == SPARSE_F32) {
+    if (a.block_size == 1)
+      score_dot_kernel<float, 1><<<grid, kDotThreads, 0, s>>>(a, p.scores, p.hist, p.n_units);
+    else
+      score_dot_kernel<float, 64><<<grid, kDotThreads, 0, s>>>(a, p.scores, p.hist, p.n_units);
+  } else {
+    if (a.block_size == 1)
+      score_dot_kernel<uint16_t, 1><<<grid, kDotThreads, 0, s>>>(a, p.scores, p.hist, p.n_units);
+    else
+      score_dot_kernel<uint16_t, 64><<<grid, kDotThreads, 0, s>>>(a, p.scores, p.hist, p.n_units);
+  }
+  return hipGetLastError();
+}
+
+// ========================================================================
+// LIGHTNING: s_t = scale_t * sum_h w_h * max(0, q_h . k8_t)
+// (scale_t > 0 factors out of the ReLU).  The q.K tile is dense, so it runs
+// on MFMA: v_mfma_f32_32x32x16_bf16 with A = q (32 heads x 16 dims), B = the
+// fp8 keys converted exactly to bf16 in registers (16 dims x 32 tokens).
+// Lane l of a wave owns token (l % 32) of a 32-token tile and dims
+// [64*(l/32), 64*(l/32)+64) of its 128-byte key: 4 x 16-byte loads.  The
+// K-dim order inside the MFMA is permuted the same way for q and k, which
+// leaves the dot products unchanged.  The accumulator of lane l holds heads
+// 32*mt + 8*jj + 4*(l/32) + ii for token l % 32, so the weighted ReLU sum is
+// lane-local up to one exchange between the two halves of the wave.
+// ========================================================================
+constexpr int kLtThreads = 256;
+constexpr int kLtTilesPerWave = 16;
+constexpr int kLtTokensPerWG = (kLtThreads / kWave) * kLtTilesPerWave * 32;
+
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
+  bf16x2 a0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+  bf16x2 a1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+  bf16x2 a2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+  bf16x2 a3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+  bf16x8 r;
+  r[0] = a0[0]; r[1] = a0[1]; r[2] = a1[0]; r[3] = a1[1];
+  r[4] = a2[0]; r[5] = a2[1]; r[6] = a3[0]; r[7] = a3[1];
+  return r;
+}
+
+template <int H>
+__global__ __launch_bounds__(kLtThreads) void score_lightning_kernel(
+    sparse_index_args a, float* __restrict__ scores, uint32_t* hist,
+    int n_units) {
+  constexpr int MT = H / 32;  // 32-head MFMA row tiles
+  __shared__ uint32_t hist_s[kHistBins];
+  LdsHist lh{hist_s};
+  const int b = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
+  const int half = lane >> 5;
+  const int col = lane & 31;
+  const int n = a.n;
+  const int valid = valid_len(a.seq_lens, b, n);
+  if (hist) lh.clear(kLtThreads);
+
+  // A operands: q[32*mt + col][64*half + 8*s + 0..7]
+  bf16x8 qa[MT][8];
+  const uint16_t* qb = (const uint16_t*)a.q + (int64_t)b * a.q_stride_b;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const uint16_t* qh = qb + (int64_t)(32 * mt + col) * a.q_stride_h + 64 * half;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qa[mt][s] = *(const bf16x8*)(qh + 8 * s);
+  }
+  // weights of the heads this lane's accumulators hold
+  float wv[MT][16];
+  const float* wb = a.head_w + (int64_t)b * a.w_stride_b;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii)
+        wv[mt][4 * jj + ii] = wb[32 * mt + 8 * jj + 4 * half + ii];
+
+  const uint8_t* kb = (const uint8_t*)a.keys + (int64_t)b * a.k_stride_b;
+  const float* ksb = a.k_scale + (int64_t)b * a.ks_stride_b;
+  float* srow = scores + (int64_t)b * n_units;
+  const int t0 = blockIdx.x * kLtTokensPerWG + wid * 32;
+  constexpr int kStride = (kLtThreads / kWave) * 32;
+
+  auto load_tile = [&](int tile_base, uint4* raw) {
+    int t = tile_base + col;
+    t = t < n ? t : n - 1;
+    const uint4* p = (const uint4*)(kb + (int64_t)t * a.k_stride_t + 64 * half);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) raw[i] = p[i];
+  };
+
+  uint4 cur[4], nxt[4];
+  if (t0 < n) load_tile(t0, cur);
+  for (int it = 0; it < kLtTilesPerWave; ++it) {
+    const int tb = t0 + it * kStride;
+    if (tb >= n) break;
+    const int tn = tb + kStride;
+    if (it + 1 < kLtTilesPerWave && tn < n) load_tile(tn, nxt);
+    const int t = tb + col;
+    const float sc = ksb[t < n ? t : n - 1];
+
+    f32x16 acc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[mt][e] = 0.f;
+    const uint32_t* w = (const uint32_t*)cur;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      bf16x8 kv = fp8x8_to_bf16(w[2 * s], w[2 * s + 1]);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mt][s], kv, acc[mt], 0, 0, 0);
+    }
+    float sum = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sum = fmaf(wv[mt][e], fmaxf(acc[mt][e], 0.f), sum);
+    // lanes l and l^32 hold the two halves of the heads of the same token
+    float other = swap_halves(sum);
+    float total = half ? other + sum : sum + other;
+    float s_t = sc * total;
+    if (t >= valid) s_t = -__builtin_huge_valf();
+    if (half == 0 && t < n) {
+      srow[t] = s_t;
+      if (hist && t < valid) lh.add(s_t);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) cur[i] = nxt[i];
+  }
+  if (hist) {
+    __syncthreads();
+    lh.flush(hist + (int64_t)b * kHistBins, kLtThreads);
+  }
+}
+
+hipError_t launch_score_lightning(const ScorePlan& p, hipStream_t s) {
+  const sparse_index_args& a = *p.a;
+  dim3 grid((a.n + kLtTokensPerWG - 1) / kLtTokensPerWG, a.batch);
+  if (a.n_heads == 64)
+    score_lightning_kernel<64><<<grid, kLtThreads, 0, s>>>(a, p.scores, p.hist, p.n_units);
+  else
+    score_lightning_kernel<32><<<grid, kLtThreads, 0, s>>>(a, p.scores, p.hist, p.n_units);
+  return hipGetLastError();
+}
+
+// ========================================================================
+// Fathom read depth: one workgroup per (request, KV head), one thread per
+// (channel, plane) gain.  All arithmetic that decides the allocation is
+// float64 with a fixed operation order: q_bar = ((q_0 + q_1) + ...),
+// imp = (q_bar * q_bar) * var, gain = imp * 4^-j (an exact power-of-two
+// scaling); those are exact for bf16 queries and fp32 variances, so the
+// ranking (gain desc, channel asc, plane asc) is reproducible bit for bit.
+// The workgroup also turns the depths into the scan's plane weights
+// W_{c,j} = q_bar_c * cell_c * 2^(3-j) for read planes and the constant
+// sum_c q_bar_c * (zero_c + cell_c * 2^(3 - t_c)).
+// ========================================================================
+constexpr int kDepthThreads = 512;  // D = 128 channels x 4 planes
+
+__global__ __launch_bounds__(kDepthThreads) void read_depth_kernel(
+    sparse_index_args a, int8_t* __restrict__ depth, float* __restrict__ plane_w,
+    float* __restrict__ score_c) {
+  __shared__ double gain_s[kDepthThreads];
+  __shared__ double qbar_s[128];
+  __shared__ int taken_s[kDepthThreads];
+  __shared__ double cterm_s[128];
+  const int h = blockIdx.x;
+  const int b = blockIdx.y;
+  const int D = a.head_dim;
+  const int Hkv = a.n_kv_heads;
+  const int G = a.n_heads / Hkv;
+  const int tid = threadIdx.x;
+  const int c = tid >> 2;
+  const int j = tid & 3;
+  const int64_t hd = ((int64_t)b * Hkv + h) * D;
+  if (tid < D) {
+    const uint16_t* q0 = (const uint16_t*)a.q + (int64_t)b * a.q_stride_b +
+                         (int64_t)(h * G) * a.q_stride_h;
+    double acc = (double)bf16_bits_to_f32(q0[tid]);
+    for (int gq = 1; gq < G; ++gq)
+      acc = __dadd_rn(acc, (double)bf16_bits_to_f32(q0[(int64_t)gq * a.q_stride_h + tid]));
+    qbar_s[tid] = acc;
+  }
+  __syncthreads();
+  if (c < D) {
+    double qb = qbar_s[c];
+    double imp = __dmul_rn(__dmul_rn(qb, qb), (double)a.chan_var[hd + c]);
+    gain_s[tid] = ldexp(imp, -2 * j);
+  }
+  __syncthreads();
+  int taken = 0;
+  if (c < D) {
+    const double g = gain_s[tid];
+    int rank = 0;
+    const int tot = 4 * D;
+    for (int o = 0; o < tot; ++o) {
+      double go = gain_s[o];
+      // o precedes tid in (gain desc, channel asc, plane asc); index order
+      // o < tid is exactly (channel, plane) ascending
+      rank += (go > g) || (go == g && o < tid);
+    }
+    taken = rank < a.bit_budget;
+  }
+  taken_s[tid] = taken;
+  __syncthreads();
+  if (tid < D) {
+    int t = taken_s[4 * tid] + taken_s[4 * tid + 1] + taken_s[4 * tid + 2] +
+            taken_s[4 * tid + 3];
+    depth[hd + tid] = (int8_t)t;
+    double qb = qbar_s[tid];
+    double cell = (double)a.chan_scale[hd + tid];
+    double zero = (double)a.chan_zero[hd + tid];
+    cterm_s[tid] = qb * (zero + cell * ldexp(1.0, 3 - t));
+  }
+  if (plane_w && c < D) {
+    double qb = qbar_s[c];
+    double cell = (double)a.chan_scale[hd + c];
+    // weight of plane j of channel c when it is read (0 otherwise)
+    plane_w[hd * 4 + tid] = taken ? (float)(qb * cell * ldexp(1.0, 3 - j)) : 0.f;
+  }
+  __syncthreads();
+  if (score_c && tid == 0) {
+    double s = 0.0;
+    for (int i = 0; i < D; ++i) s += cterm_s[i];
+    score_c[(int64_t)b * Hkv + h] = (float)s;
+  }
+}
+
+hipError_t launch_read_depth(const sparse_index_args* a, int8_t* depth,
+                             float* plane_w, float* score_c, hipStream_t s) {
+  dim3 grid(a->n_kv_heads, a->batch);
+  read_depth_kernel<<<grid, kDepthThreads, 0, s>>>(*a, depth, plane_w, score_c);
+  return hipGetLastError();
+}
+
+// ========================================================================
+// Fathom plane-prefix scan.  Thread = one 32-token word column of a
+// (request, KV head); for each read plane (c, j) it loads that plane's word
+// (coalesced across threads) and adds W_{c,j} to the tokens whose bit is
+// set.  The list of read planes is compacted once per workgroup in LDS.
+// ========================================================================
+constexpr int kBpThreads = 256;
+
+__global__ __launch_bounds__(kBpThreads) void score_bitplane_kernel(
+    sparse_index_args a, const float* __restrict__ plane_w,
+    const float* __restrict__ score_c, float* __restrict__ scores,
+    uint32_t* hist, int n_units) {
+  __shared__ uint32_t hist_s[kHistBins];
+  __shared__ int plist_s[512];
+  __shared__ float pw_s[512];
+  __shared__ int np_s;
+  LdsHist lh{hist_s};
+  const int h = blockIdx.y;
+  const int b = blockIdx.z;
+  const int D = a.head_dim;
+  const int Hkv = a.n_kv_heads;
+  const int n = a.n;
+  const int nw = (n + 31) / 32;
+  const int valid = valid_len(a.seq_lens, b, n);
+  const int64_t hd = ((int64_t)b * Hkv + h) * D;
+  if (hist) lh.clear(kBpThreads);
+  if (threadIdx.x == 0) {
+    int cnt = 0;
+    for (int i = 0; i < 4 * D; ++i) {
+      float wgt = plane_w[hd * 4 + i];
+      // read planes are exactly those with a recorded weight slot; a zero
+      // weight adds nothing, so skipping it leaves the score unchanged
+      if (wgt != 0.f) { plist_s[cnt] = i; pw_s[cnt] = wgt; ++cnt; }
+    }
+    np_s = cnt;
+  }
+  __syncthreads();
+  const int np = np_s;
+  const float c0 = score_c[(int64_t)b * Hkv + h];
+  const uint32_t* pl = a.planes + hd * 4 * (int64_t)nw;
+  const int w = blockIdx.x * kBpThreads + threadIdx.x;
+  float* srow = scores + ((int64_t)b * Hkv + h) * n_units;
+  if (w < nw) {
+    float acc[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) acc[i] = c0;
+    for (int p = 0; p < np; ++p) {
+      uint32_t word = pl[(int64_t)plist_s[p] * nw + w];
+      float wgt = pw_s[p];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) acc[i] += ((word >> i) & 1u) ? wgt : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      int t = 32 * w + i;
+      float s = t < valid ? acc[i] : -__builtin_huge_valf();
+      if (t < n) {
+        srow[t] = s;
+        if (hist && t < valid) lh.add(s);
+      }
+    }
+  }
+  if (hist) {
+    __syncthreads();
+    lh.flush(hist + ((int64_t)b * Hkv + h) * kHistBins, kBpThreads);
+  }
+}
+
+hipError_t launch_score_bitplane(const ScorePlan& p, hipStream_t s) {
+  const sparse_index_args& a = *p.a;
+  const int nw = (a.n + 31) / 32;
+  dim3 grid((nw + kBpThreads - 1) / kBpThreads, a.n_kv_heads, a.batch);
+  score_bitplane_kernel<<<grid, kBpThreads, 0, s>>>(a, p.plane_w, p.score_c,
+                                                   p.scores, p.hist, p.n_units);
+  return hipGetLastError();
+}
+
+}  // namespace sd

@@ -41,9 +41,10 @@ def _pad_scores(s: np.ndarray, valid: int, n_units: int) -> np.ndarray:
     return out
 
 
-def dot_step(arr: dict, p: dict) -> dict:
+def dot_step(arr: dict, p: dict, sel_in: np.ndarray | None = None) -> dict:
     """Head-summed dot index over the K cache itself, GQA attention (fp32 or
-    bf16 inputs).  p: n, k, hq, hkv, dtype, seq_lens."""
+    bf16 inputs).  p: n, k, hq, hkv, dtype, seq_lens.  With sel_in
+    ([B][1][k]) the given selection is attended instead of the top-k."""
     q = _dec(arr["q"], p["dtype"])
     K = _dec(arr["k_cache"], p["dtype"])
     V = _dec(arr["v_cache"], p["dtype"])
@@ -57,7 +58,7 @@ def dot_step(arr: dict, p: dict) -> dict:
         # index keys: KV head 0 of the K cache (one KV head in this kind)
         s = O.score_dot_headsum(q[b], K[b, :valid, 0, :])
         s = _pad_scores(s, valid, p["n"])
-        sel = O.topk(s, p["k"], valid)
+        sel = O.topk(s, p["k"], valid) if sel_in is None else sel_in[b, 0]
         toks = O.expand_selection(sel, 1, valid)
         out = np.zeros((Hq, V.shape[3]))
         lse = np.zeros(Hq)
@@ -97,9 +98,11 @@ def lightning_scores(arr: dict, p: dict, b: int) -> np.ndarray:
     return _pad_scores(s, valid, p["n"])
 
 
-def lightning_step(arr: dict, p: dict, requests=None) -> dict:
+def lightning_step(arr: dict, p: dict, requests=None,
+                   sel_in: np.ndarray | None = None) -> dict:
     """Lightning-indexer fp8 scores, top-k tokens, MLA attention over the
-    selected latent rows (key = the whole row, value = its first d_v dims)."""
+    selected latent rows (key = the whole row, value = its first d_v dims).
+    With sel_in ([B][1][k]) scoring is skipped and that selection attended."""
     B = arr["q"].shape[0]
     d_qk, d_v = p["d_qk"], p["d_v"]
     scale = p.get("sm_scale", 1.0 / math.sqrt(d_qk))
@@ -107,8 +110,12 @@ def lightning_step(arr: dict, p: dict, requests=None) -> dict:
     scores, sels, outs, lses = [], [], [], []
     for b in reqs:
         valid = _valid(p, b)
-        s = lightning_scores(arr, p, b)
-        sel = O.topk(s, p["k"], valid)
+        if sel_in is None:
+            s = lightning_scores(arr, p, b)
+            sel = O.topk(s, p["k"], valid)
+        else:
+            s = np.zeros(p["n"])
+            sel = sel_in[b, 0]
         toks = O.expand_selection(sel, 1, valid)
         rows = latent_rows(arr, p, b, toks)
         q = O.decode_bf16(arr["q"][b])
@@ -186,7 +193,8 @@ def block_step(arr: dict, p: dict, sel_in: np.ndarray | None = None) -> dict:
     return res
 
 
-def fathom_step(arr: dict, p: dict, requests=None) -> dict:
+def fathom_step(arr: dict, p: dict, requests=None,
+                sel_in: np.ndarray | None = None) -> dict:
     """Fathom scan: per (request, KV head) read depth by reverse
     water-filling, plane-prefix scores, top-k tokens per KV head, bf16 GQA
     attention of that head's query group over its own selection."""
@@ -208,7 +216,7 @@ def fathom_step(arr: dict, p: dict, requests=None) -> dict:
                                O.decode_f32(arr["chan_zero"][b, h]),
                                O.decode_f32(arr["chan_scale"][b, h]), t)
             s = _pad_scores(s, valid, p["n"])
-            sel = O.topk(s, p["k"], valid)
+            sel = O.topk(s, p["k"], valid) if sel_in is None else sel_in[b, h]
             srow.append(s)
             selrow.append(sel)
             drow.append(t)
