@@ -1,0 +1,256 @@
+"""Decode-step benchmark of the sparse decode library on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
+
+A step is one whole decode step (index scan + top-k + sparse attention) of
+the named workload over one batch of synthetic inputs already resident in
+HBM, enqueued through the C ABI and replayed as a HIP graph.  Two input sets
+with different seeds alternate so that the timed window never re-reads a
+set that the 256 MB last-level cache could hold.  Prints ONE JSON line.
+
+The default workload is the lightning-indexer decode at 128K context: batch
+32, 131072 cached tokens, 64 index heads over an fp8 K-index with per-token
+scales, top-2048, 128-head MLA attention over 576-wide bf16 latent rows in
+64-token pages.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
+METRIC = "sparse decode steps/s (score+top-k+attn) at 128K ctx; % of HBM peak BW"
+
+
+def algorithmic_bytes(w) -> dict:
+    """Bytes the method must move per step (no score scratch)."""
+    B, n, k = w.B, w.n, w.k
+    out = {}
+    if w.kind == "lightning":
+        out["k_index"] = B * n * (w.idx_dim + 4)            # fp8 key + fp32 scale
+        out["selected_kv"] = B * k * w.d_qk * 2             # latent rows, read once
+        out["q_w"] = B * w.idx_heads * (w.idx_dim * 2 + 4) + B * w.hq * w.d_qk * 2
+        out["out"] = B * w.hq * (w.d_v + 1) * 4
+        out["idx_pt"] = B * k * 4 * 2                       # top-k ids + page-table reads
+    elif w.kind == "block":
+        out["k_index"] = B * n * w.idx_dim * 2
+        out["selected_kv"] = w.layers * B * k * w.block * w.hkv * (w.d_qk + w.d_v) * 2
+        out["q_w"] = B * w.idx_heads * w.idx_dim * 2 + w.layers * B * w.hq * w.d_qk * 2
+        out["out"] = w.layers * B * w.hq * (w.d_v + 1) * 4
+        out["idx_pt"] = B * k * 4
+    elif w.kind == "fathom":
+        out["k_index"] = B * w.hkv * (w.budget * n // 8 + w.d_qk * 12)  # planes read + zero/scale/var
+        out["selected_kv"] = B * w.hkv * k * (w.d_qk + w.d_v) * 2
+        out["q_w"] = B * w.hq * w.d_qk * 2
+        out["out"] = B * w.hq * (w.d_v + 1) * 4
+        out["idx_pt"] = B * w.hkv * k * 4
+    elif w.kind == "dot":
+        out["k_index"] = B * n * w.d_qk * 4
+        out["selected_kv"] = B * k * w.hkv * (w.d_qk + w.d_v) * 4
+        out["q_w"] = B * w.hq * w.d_qk * 4
+        out["out"] = B * w.hq * (w.d_v + 1) * 4
+        out["idx_pt"] = B * k * 4
+    out["total"] = sum(out.values())
+    return out
+
+
+def score_kernel_bytes(w) -> int:
+    """Algorithmic bytes of one launch of the index-scan kernel."""
+    if w.kind == "lightning":
+        return w.B * w.n * (w.idx_dim + 4)
+    if w.kind == "block":
+        return w.B * w.n * w.idx_dim * 2
+    if w.kind == "fathom":
+        return w.B * w.hkv * w.budget * w.n // 8
+    return w.B * w.n * w.d_qk * 4
+
+
+def cpu_baseline(w, inp, requests: int) -> dict:
+    """The oracle (as it stands) on a bounded sample of the same workload."""
+    import numpy as np
+    import torch
+
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    import synth  # noqa: F401
+    from oracle import step as S
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        threads = 1
+    p = {"n": w.n, "k": w.k, "hq": w.hq, "hkv": w.hkv, "dtype": w.dtype,
+         "seq_lens": w.seq_lens, "page": w.page, "block": w.block, "budget": w.budget,
+         "d_qk": w.d_qk, "d_v": w.d_v}
+    reqs = list(range(min(requests, w.B)))
+    if w.kind != "lightning":
+        raise ValueError("cpu baseline sample is defined for the lightning workload")
+    t_total = 0.0
+    for b in reqs:
+        # request b's inputs only; its pages renumbered 0..n_pages-1
+        pt = inp["page_table"][b].long()
+        arr = {
+            "q_idx": synth.host_view(inp["q_idx"][b:b + 1]),
+            "head_w": synth.host_view(inp["head_w"][b:b + 1]),
+            "k8": synth.host_view(inp["k8"][b:b + 1]),
+            "k_scale": synth.host_view(inp["k_scale"][b:b + 1]),
+            "q": synth.host_view(inp["q"][b:b + 1]),
+            "kv_pool": synth.host_view(inp["kv_pool"].index_select(0, pt)),
+            "page_table": np.arange(pt.numel(), dtype=np.int32)[None, :],
+        }
+        t0 = time.perf_counter()
+        S.lightning_step(arr, p)
+        t_total += time.perf_counter() - t0
+    per_req = t_total / len(reqs)
+    return {"value": 1.0 / (per_req * w.B), "unit": "steps/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{len(reqs)} of {w.B} requests at full context "
+                      f"(n={w.n}, k={w.k}), oracle seconds scaled by {w.B}/{len(reqs)}; "
+                      f"host cpu_count={os.cpu_count()}"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="lightning_128k")
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--cpu-requests", type=int, default=4)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--misses", type=int, default=1, help="hot-buffer workloads: 1 = 20%% misses")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(requests shard by batch with no exchange; see the sharding notes)",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    import synth
+    from synth.gen import build_hot_buffer
+    import indexer_top_sparse_amd as isa
+    from indexer_top_sparse_amd.runner import StepRunner
+
+    isa.lib()  # fail loudly if the HIP library is missing
+    w = synth.get(args.config)
+    dev = "cuda"
+    print(f"[bench] generating inputs for {w.name}", file=sys.stderr, flush=True)
+    sets = []
+    for s in range(2):
+        ws = w.with_(seed=w.seed + 100 * s)
+        inp = synth.make_inputs(ws, dev)
+        hot = None
+        if w.hot:
+            # the selection the step will make decides which rows are hot
+            sel = _selection_for_hot(inp, ws, dev)
+            hw = ws.with_(miss_rate=w.miss_rate if args.misses else 0.0)
+            hot = build_hot_buffer(dict(inp, workload=hw), sel, dev)
+        sets.append((inp, StepRunner(inp, hot=hot)))
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    # warmup (eager), then capture one graph per input set
+    for i in range(max(args.warmup, 1)):
+        sets[i % 2][1].run()
+    torch.cuda.synchronize()
+    graphs = []
+    if not args.no_graph:
+        for _, r in sets:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                r.run()
+            graphs.append(g)
+        for i in range(max(args.warmup, 1)):
+            graphs[i % 2].replay()
+    torch.cuda.synchronize()
+
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        if graphs:
+            graphs[i % 2].replay()
+        else:
+            sets[i % 2][1].run()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms = 1e3 * elapsed / args.steps
+    steps_s = args.steps / elapsed
+
+    # dominant kernel: the index scan, timed with HIP events on its stream
+    reps = 20
+    r0 = sets[0][1]
+    r0.index_scores()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for i in range(reps):
+        sets[i % 2][1].index_scores()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    score_ms = ev0.elapsed_time(ev1) / reps
+    kb = score_kernel_bytes(w)
+    achieved = kb / (score_ms * 1e-3) / 1e9
+
+    ab = algorithmic_bytes(w)
+    line = {
+        "metric": METRIC,
+        "value": round(steps_s, 2),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.B, "context": w.n, "top_k": w.k,
+                   "index_heads": w.idx_heads, "attn_heads": w.hq, "kv_heads": w.hkv,
+                   "d_qk": w.d_qk, "d_v": w.d_v, "page": w.page, "block": w.block,
+                   "bit_budget": w.budget, "hot_tokens": w.hot,
+                   "miss_rate": (w.miss_rate if args.misses else 0.0) if w.hot else None,
+                   "graph": not args.no_graph},
+        "step_bytes": ab["total"],
+        "step_GBps": round(ab["total"] / (ms * 1e-3) / 1e9, 1),
+        "step_hbm_frac": round(ab["total"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "roofline": {"kernel": f"index scan ({w.kind})", "bound": "hbm",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "avg_launch_ms": round(score_ms, 5),
+                     "bytes_per_launch": kb},
+    }
+    if not args.no_cpu and w.kind == "lightning" and not w.hot:
+        print("[bench] timing the oracle on a sample", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(w, sets[0][0], args.cpu_requests)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def _selection_for_hot(inp, w, dev):
+    """The step's own selection (indexer + top-k through the library), used
+    only to decide which rows start in the hot buffer."""
+    import torch
+    import indexer_top_sparse_amd as isa
+
+    ia = isa.lightning_index_args(inp["q_idx"], inp["head_w"], inp["k8"], inp["k_scale"],
+                                  inp.get("seq_lens"))
+    scores = torch.empty((w.B, w.n), dtype=torch.float32, device=dev)
+    ws = isa.workspace(max(isa.sparse_workspace_size(ia, None, w.k),
+                           isa.sparse_topk_workspace_size(w.B, w.n, w.k)), dev)
+    isa.sparse_index_score(ia, scores, ws)
+    sel = torch.empty((w.B, w.k), dtype=torch.int32, device=dev)
+    isa.sparse_topk(scores, w.k, sel, None, inp.get("seq_lens"), 1, ws)
+    torch.cuda.synchronize()
+    return sel
+
+
+if __name__ == "__main__":
+    sys.exit(main())
