@@ -76,29 +76,31 @@ IndexLayout index_layout(const sparse_index_args& a, bool with_scores) {
   return L;
 }
 
-// Fixed split heuristic (no runtime tuning): enough workgroups to cover
-// the 256 compute units about twice, but never fewer than 64 tokens per
-// split.
+// Fixed split heuristic (no runtime tuning): enough workgroups to fill the
+// 256 compute units (512 for the lighter 4-wave kernels), never fewer than
+// min_tok tokens per split, and never more than 2048 tokens per split (the
+// kernels resolve a split's rows into a 2048-entry LDS table).
 int attn_splits(const sparse_attn_args& a, int k_tokens) {
   if (k_tokens <= 0) return 1;
-  int groups;
-  int min_tok;
+  int groups, min_tok, target;
   if (a.dtype == SPARSE_F32) {
     groups = a.n_q_heads;
     min_tok = 64;
+    target = 256;
   } else if (a.d_qk == 576) {
     groups = a.n_q_heads / 32;
     min_tok = 256;
+    target = 256;
   } else {
     groups = a.n_kv_heads;
     min_tok = 64;
+    target = 512;
   }
   const int64_t base = (int64_t)std::max(a.batch, 1) * std::max(groups, 1);
-  int s = (int)ceil_div(512, base);
+  int64_t s = ceil_div(target, base);
   s = std::min<int64_t>(s, std::max<int64_t>(1, k_tokens / min_tok));
-  s = std::max(s, 1);
-  if (a.dtype == SPARSE_F32) s = std::max<int>(s, (int)ceil_div(k_tokens, 2048));
-  return s;
+  s = std::max<int64_t>(s, ceil_div(k_tokens, 2048));
+  return (int)std::max<int64_t>(s, 1);
 }
 
 struct AttnLayout {

@@ -158,39 +158,48 @@ hipError_t launch_attn_f32(const AttnPlan& p, hipStream_t s) {
 }
 
 // =================================================================== bf16
-constexpr int kAttnThreads = 256;
-constexpr int kTT = 32;  // tokens per tile
+constexpr int kTT = 32;           // tokens per tile
+constexpr int kStages = 3;        // tiles in flight (register prefetch)
+constexpr int kMaxSplitTok = 2048;
 
-template <int DQK, int DV, int HG, bool LATENT>
+template <int DQK, int DV, int HG, bool LATENT, int NW>
 struct AttnCfg {
+  static constexpr int kNT = 64 * NW;                   // threads
   static constexpr int kRowK = DQK + 8;                 // LDS row stride (elements)
   static constexpr int kRowV = LATENT ? kRowK : DV + 8;
   static constexpr int kCprK = DQK * 2 / 16;            // 16-byte chunks per K row
   static constexpr int kCprV = LATENT ? 0 : DV * 2 / 16;
   static constexpr int kChunks = kTT * (kCprK + kCprV);
-  static constexpr int kNch = (kChunks + kAttnThreads - 1) / kAttnThreads;
-  static constexpr int kKSteps = DQK / 32;              // QK k-steps
+  static constexpr int kNch = (kChunks + kNT - 1) / kNT;
+  static constexpr int kKS = DQK / 32;                  // QK k-steps
   static constexpr int kMT = HG / 16;                   // head m-tiles
   static constexpr int kNTQ = kTT / 16;                 // QK token n-tiles
-  static constexpr int kWC = DV / 4;                    // PV columns per wave
+  static constexpr int kPairs = kMT * kNTQ;
+  static constexpr int kKSplit = NW / kPairs;           // waves sharing one S tile
+  static constexpr int kKSW = kKS / kKSplit;            // k-steps per wave
+  static constexpr int kWC = DV / NW;                   // PV columns per wave
   static constexpr int kCPL = kWC / 16;                 // PV columns per lane
-  static constexpr int kTPR = kAttnThreads / HG;        // softmax threads per row
+  static constexpr int kTPR = kNT / HG;                 // softmax threads per row
   static constexpr int kEPT = kTT / kTPR;               // softmax entries per thread
-  static_assert(kMT * kNTQ <= 4, "QK tiles exceed the waves");
+  static_assert(NW % kPairs == 0 && kKS % kKSplit == 0, "QK work split");
   static_assert(kCPL == 2 || kCPL == 4 || kCPL == 8, "PV strip width");
+  static_assert(kTPR <= 64 && kEPT >= 1, "softmax split");
 };
 
-template <int DQK, int DV, int HG, bool LATENT>
-__global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(AttnPlan p) {
-  using C = AttnCfg<DQK, DV, HG, LATENT>;
+// Row pointer word: the 16-byte aligned address of the token's K row, with
+// bit 0 set when the slot is masked (then the address is a finite dummy row
+// so that every load in the pipeline is unconditional).
+template <int DQK, int DV, int HG, bool LATENT, int NW>
+__global__ __launch_bounds__(64 * NW) void attn_bf16_kernel(AttnPlan p) {
+  using C = AttnCfg<DQK, DV, HG, LATENT, NW>;
   __shared__ __attribute__((aligned(16))) uint16_t ks_s[kTT * C::kRowK];
   __shared__ __attribute__((aligned(16))) uint16_t vs_s[LATENT ? 8 : kTT * C::kRowV];
-  __shared__ float s_s[HG * kTT];
+  __shared__ float s_s[C::kKSplit * HG * kTT];
   __shared__ __attribute__((aligned(16))) uint16_t p_s[HG * (kTT + 8)];
   __shared__ float alpha_s[HG];
   __shared__ float m_s[HG];
   __shared__ float l_s[HG];
-  __shared__ int tok_s[kTT];
+  __shared__ uint64_t rowp_s[kMaxSplitTok];
 
   const sparse_attn_args& A = p.a;
   const int split = blockIdx.x;
@@ -200,8 +209,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(AttnPlan p) {
   const int lane = tid & 63;
   const int wid = tid >> 6;
   const int G = A.n_q_heads / A.n_kv_heads;
-  // head group: MLA-style (one KV head, HG heads per group) or one KV head
-  // per group with its G <= HG query heads (rows past G are padding)
+  // head group: latent rows (one KV head, HG query heads per group) or one
+  // KV head per group with its G <= HG query heads (rows past G are padding)
   const int kvh = (A.n_kv_heads == 1) ? 0 : grp;
   const int head0 = (A.n_kv_heads == 1) ? grp * HG : grp * G;
   const int greal = (A.n_kv_heads == 1) ? HG : G;
@@ -211,55 +220,64 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(AttnPlan p) {
   const int tps = (p.k_tokens + p.splits - 1) / p.splits;
   const int j0 = split * tps;
   const int j1 = min(j0 + tps, p.k_tokens);
-  const int ntiles = j1 > j0 ? (j1 - j0 + kTT - 1) / kTT : 0;
+  const int cnt = max(0, j1 - j0);
+  const int ntiles = (cnt + kTT - 1) / kTT;
   const int64_t stage_base = ((int64_t)b * p.sel_heads + selrow_i) * p.k_tokens;
   RowAddr ra{A};
+  const int64_t vdelta = LATENT ? 0 : (const char*)A.v_cache - (const char*)A.k_cache;
+
+  // ---- resolve every row of the split once (selection -> page / slot)
+  const uint64_t dummy =
+      ((uint64_t)(A.hot_slot ? (const char*)A.hot_kv + (int64_t)b * A.hot_stride_b * 2
+                             : (const char*)A.k_cache)) | 1ull;
+  for (int i = tid; i < cnt; i += C::kNT) {
+    const int j = j0 + i;
+    const int t = sel_token(selrow, j, p.sel_unit, valid);
+    rowp_s[i] = t >= 0 ? (uint64_t)ra.k_row(b, kvh, t, stage_base + j, p.staging, 2)
+                       : dummy;
+  }
+  __syncthreads();
 
   // ---- q operands (A of QK): head 16*mt + (lane%16), dims 32s + 8(lane/16)
-  const int qmt = wid / C::kNTQ;
-  const int qnt = wid % C::kNTQ;
-  const bool qk_wave = qmt < C::kMT;
-  bf16x8 qa[C::kKSteps];
+  const int pair = wid % C::kPairs;
+  const int kpart = wid / C::kPairs;
+  const int qmt = pair / C::kNTQ;
+  const int qnt = pair % C::kNTQ;
+  bf16x8 qa[C::kKSW];
   {
-    const int hr = (qk_wave ? qmt : 0) * 16 + (lane & 15);
-    const bool real = qk_wave && hr < greal;
+    const int hr = qmt * 16 + (lane & 15);
+    const bool real = hr < greal;
     const uint16_t* qp = (const uint16_t*)A.q + (int64_t)b * A.q_stride_b +
-                         (int64_t)(head0 + (real ? hr : 0)) * A.q_stride_h + 8 * (lane >> 4);
+                         (int64_t)(head0 + (real ? hr : 0)) * A.q_stride_h +
+                         32 * (kpart * C::kKSW) + 8 * (lane >> 4);
 #pragma unroll
-    for (int s = 0; s < C::kKSteps; ++s) {
+    for (int s = 0; s < C::kKSW; ++s) {
       if (real) qa[s] = *(const bf16x8*)(qp + 32 * s);
       else for (int e = 0; e < 8; ++e) qa[s][e] = (__bf16)0.f;
     }
   }
 
-  // ---- tile gather (registers), one tile ahead
-  uint4 pre[C::kNch];
-  auto gather = [&](int tile) {
-    const int jt = j0 + tile * kTT;
+  // ---- tile gather: kNch 16-byte chunks per thread, all loads unconditional
+  auto gather = [&](u32x4 (&pre)[C::kNch], int tile) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < C::kNch; ++i) {
-      const int q = tid + i * kAttnThreads;
-      pre[i] = make_uint4(0u, 0u, 0u, 0u);
-      if (q < C::kChunks) {
-        const bool isv = q >= kTT * C::kCprK;
-        const int qq = isv ? q - kTT * C::kCprK : q;
-        const int cpr = isv ? C::kCprV : C::kCprK;
-        const int row = qq / cpr;
-        const int cc = qq % cpr;
-        const int j = jt + row;
-        int t = (j < j1) ? sel_token(selrow, j, p.sel_unit, valid) : -1;
-        if (t >= 0) {
-          const char* base = isv ? ra.v_row(b, kvh, t, 2)
-                                 : ra.k_row(b, kvh, t, stage_base + j, p.staging, 2);
-          pre[i] = *(const uint4*)(base + 16 * cc);
-        }
-      }
+      const int q = tid + i * C::kNT;
+      const int qc = q < C::kChunks ? q : C::kChunks - 1;
+      const bool isv = qc >= kTT * C::kCprK;
+      const int qq = isv ? qc - kTT * C::kCprK : qc;
+      const int cpr = isv ? C::kCprV : C::kCprK;
+      const int row = qq / cpr;
+      const int cc = qq % cpr;
+      const int it = tile * kTT + row;
+      const uint64_t w = it < cnt ? rowp_s[it] : dummy;
+      const char* base = (const char*)(w & ~15ull) + (isv ? vdelta : 0);
+      pre[i] = *(gptr<const u32x4>)(base + 16 * cc);
     }
   };
-  auto commit = [&](int tile) {
+  auto commit = [&](const u32x4 (&pre)[C::kNch]) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < C::kNch; ++i) {
-      const int q = tid + i * kAttnThreads;
+      const int q = tid + i * C::kNT;
       if (q < C::kChunks) {
         const bool isv = q >= kTT * C::kCprK;
         const int qq = isv ? q - kTT * C::kCprK : q;
@@ -267,12 +285,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(AttnPlan p) {
         const int row = qq / cpr;
         const int cc = qq % cpr;
         uint16_t* dst = isv ? vs_s + row * C::kRowV : ks_s + row * C::kRowK;
-        *(uint4*)(dst + 8 * cc) = pre[i];
+        *(u32x4*)(dst + 8 * cc) = pre[i];
       }
-    }
-    if (tid < kTT) {
-      const int j = j0 + tile * kTT + tid;
-      tok_s[tid] = (j < j1) ? sel_token(selrow, j, p.sel_unit, valid) : -1;
     }
   };
 
@@ -291,28 +305,24 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(AttnPlan p) {
     for (int nt = 0; nt < C::kCPL; ++nt)
       for (int e = 0; e < 4; ++e) o[mt][nt][e] = 0.f;
 
-  if (ntiles > 0) gather(0);
-  for (int tile = 0; tile < ntiles; ++tile) {
-    __syncthreads();  // previous tile fully consumed
-    commit(tile);
-    __syncthreads();
-    if (tile + 1 < ntiles) gather(tile + 1);
-
-    // ---- S = scale * q K^T  (wave: 16 heads x 16 tokens)
-    if (qk_wave) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      const uint16_t* kr = ks_s + (16 * qnt + (lane & 15)) * C::kRowK + 8 * (lane >> 4);
+  auto process = [&](int tile) __attribute__((always_inline)) {
+    // ---- partial S = scale * q K^T over this wave's k-steps
+    {
+      f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+      const uint16_t* kr = ks_s + (16 * qnt + (lane & 15)) * C::kRowK +
+                           32 * (kpart * C::kKSW) + 8 * (lane >> 4);
 #pragma unroll
-      for (int s = 0; s < C::kKSteps; ++s) {
+      for (int s = 0; s < C::kKSW; ++s) {
         bf16x8 kv = *(const bf16x8*)(kr + 32 * s);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], kv, acc, 0, 0, 0);
+        if (s & 1) acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], kv, acc1, 0, 0, 0);
+        else acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], kv, acc0, 0, 0, 0);
       }
-      const int col = 16 * qnt + (lane & 15);
-      const bool ok = tok_s[col] >= 0;
+      const int colq = 16 * qnt + (lane & 15);
+      float* sp = s_s + kpart * HG * kTT;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * qmt + 4 * (lane >> 4) + i;
-        s_s[r * kTT + col] = ok ? acc[i] * A.sm_scale : -__builtin_huge_valf();
+        sp[r * kTT + colq] = acc0[i] + acc1[i];
       }
     }
     __syncthreads();
@@ -323,7 +333,13 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(AttnPlan p) {
       float tmax = -__builtin_huge_valf();
 #pragma unroll
       for (int e = 0; e < C::kEPT; ++e) {
-        sv[e] = s_s[srow * kTT + ssub * C::kEPT + e];
+        const int col = ssub * C::kEPT + e;
+        float v = 0.f;
+#pragma unroll
+        for (int kp = 0; kp < C::kKSplit; ++kp) v += s_s[(kp * HG + srow) * kTT + col];
+        const int it = tile * kTT + col;
+        const bool ok = it < cnt && !(rowp_s[it] & 1ull);
+        sv[e] = ok ? v * A.sm_scale : -__builtin_huge_valf();
         tmax = fmaxf(tmax, sv[e]);
       }
 #pragma unroll
@@ -350,23 +366,18 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(AttnPlan p) {
 
     // ---- O = alpha * O + P V  (wave: all heads x kWC columns)
     {
-      float al[C::kMT][4];
 #pragma unroll
       for (int mt = 0; mt < C::kMT; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) al[mt][i] = alpha_s[16 * mt + 4 * (lane >> 4) + i];
+        for (int i = 0; i < 4; ++i) {
+          const float al = alpha_s[16 * mt + 4 * (lane >> 4) + i];
 #pragma unroll
-      for (int mt = 0; mt < C::kMT; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < C::kCPL; ++nt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) o[mt][nt][i] *= al[mt][i];
-
+          for (int nt = 0; nt < C::kCPL; ++nt) o[mt][nt][i] *= al;
+        }
       bf16x8 pa[C::kMT];
 #pragma unroll
       for (int mt = 0; mt < C::kMT; ++mt)
         pa[mt] = *(const bf16x8*)(p_s + (16 * mt + (lane & 15)) * (kTT + 8) + 8 * (lane >> 4));
-
       // V strip: tokens 8*(lane/16) + i, columns wid*kWC + kCPL*(lane%16) ..
       const uint16_t* vbase = (LATENT ? ks_s : vs_s) + (8 * (lane >> 4)) * C::kRowV +
                               wid * C::kWC + C::kCPL * (lane & 15);
@@ -398,6 +409,34 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(AttnPlan p) {
           o[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[mt], vb, o[mt][nt], 0, 0, 0);
       }
     }
+  };
+
+  // ---- pipeline: tile t is gathered kStages-1 tiles ahead into buffer
+  // t % kStages; the loop runs whole groups of kStages tiles (a tile past
+  // the split is fully masked and leaves the state unchanged, and its loads
+  // hit the dummy row).
+  static_assert(kStages == 3, "the pipeline below is written for 3 stages");
+  u32x4 pre0[C::kNch], pre1[C::kNch], pre2[C::kNch];
+  const int groups = (ntiles + kStages - 1) / kStages;
+  gather(pre0, 0);
+  gather(pre1, 1);
+  for (int g = 0; g < groups; ++g) {
+    const int t = g * kStages;
+    gather(pre2, t + 2);
+    __syncthreads();  // the previous tile's LDS readers are done
+    commit(pre0);
+    __syncthreads();
+    process(t);
+    gather(pre0, t + 3);
+    __syncthreads();
+    commit(pre1);
+    __syncthreads();
+    process(t + 1);
+    gather(pre1, t + 4);
+    __syncthreads();
+    commit(pre2);
+    __syncthreads();
+    process(t + 2);
   }
 
   // ---- epilogue
@@ -441,10 +480,10 @@ hipError_t launch_attn_bf16(const AttnPlan& p, hipStream_t s) {
   const sparse_attn_args& a = p.a;
   if (a.d_qk == 576 && a.d_v == 512 && a.v_cache == nullptr && a.n_kv_heads == 1) {
     dim3 grid(p.splits, a.n_q_heads / 32, a.batch);
-    attn_bf16_kernel<576, 512, 32, true><<<grid, kAttnThreads, 0, s>>>(p);
+    attn_bf16_kernel<576, 512, 32, true, 8><<<grid, 512, 0, s>>>(p);
   } else if (a.d_qk == 128 && a.d_v == 128 && a.v_cache != nullptr) {
     dim3 grid(p.splits, a.n_kv_heads, a.batch);
-    attn_bf16_kernel<128, 128, 16, false><<<grid, kAttnThreads, 0, s>>>(p);
+    attn_bf16_kernel<128, 128, 16, false, 4><<<grid, 256, 0, s>>>(p);
   } else {
     return hipErrorInvalidValue;
   }
@@ -454,39 +493,35 @@ hipError_t launch_attn_bf16(const AttnPlan& p, hipStream_t s) {
 // ================================================================ combine
 // Merge split partials of one (request, head): M = max m_s,
 // L = sum l_s exp(m_s - M), out = sum o_s exp(m_s - M) / L, lse = M + log L.
+// One thread per output element.
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnPlan p) {
-  const int hq = blockIdx.x;
-  const int b = blockIdx.y;
   const sparse_attn_args& A = p.a;
   const int dv = A.d_v;
   const int S = p.splits;
-  const int64_t oh = (int64_t)b * A.n_q_heads + hq;
+  const int64_t total = (int64_t)A.batch * A.n_q_heads * dv;
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= total) return;
+  const int64_t oh = e / dv;
+  const int d = (int)(e % dv);
   const float* pp = p.part + oh * S * (dv + 2);
   float M = -__builtin_huge_valf();
   for (int s = 0; s < S; ++s) M = fmaxf(M, pp[s * (dv + 2) + dv]);
-  float L = 0.f;
+  float L = 0.f, acc = 0.f;
   for (int s = 0; s < S; ++s) {
-    float m = pp[s * (dv + 2) + dv];
-    float l = pp[s * (dv + 2) + dv + 1];
-    if (l > 0.f) L += l * __expf(m - M);
-  }
-  const float inv = L > 0.f ? 1.f / L : 0.f;
-  for (int d = threadIdx.x; d < dv; d += blockDim.x) {
-    float acc = 0.f;
-    for (int s = 0; s < S; ++s) {
-      float m = pp[s * (dv + 2) + dv];
-      float l = pp[s * (dv + 2) + dv + 1];
-      if (l > 0.f) acc += pp[s * (dv + 2) + d] * __expf(m - M);
+    const float l = pp[s * (dv + 2) + dv + 1];
+    if (l > 0.f) {
+      const float f = __expf(pp[s * (dv + 2) + dv] - M);
+      L += l * f;
+      acc += pp[s * (dv + 2) + d] * f;
     }
-    p.out[oh * dv + d] = acc * inv;
   }
-  if (threadIdx.x == 0 && p.lse)
-    p.lse[oh] = L > 0.f ? M + __logf(L) : -__builtin_huge_valf();
+  p.out[e] = L > 0.f ? acc / L : 0.f;
+  if (d == 0 && p.lse) p.lse[oh] = L > 0.f ? M + __logf(L) : -__builtin_huge_valf();
 }
 
 hipError_t launch_attn_combine(const AttnPlan& p, hipStream_t s) {
-  dim3 grid(p.a.n_q_heads, p.a.batch);
-  attn_combine_kernel<<<grid, 256, 0, s>>>(p);
+  const int64_t total = (int64_t)p.a.batch * p.a.n_q_heads * p.a.d_v;
+  attn_combine_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(p);
   return hipGetLastError();
 }
 

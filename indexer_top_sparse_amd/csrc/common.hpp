@@ -14,8 +14,14 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
+
+// Pointer into the global address space: loads through it compile to
+// global_load (vector memory counter only) rather than flat_load.
+template <typename T>
+using gptr = __attribute__((address_space(1))) T*;
 
 // ---------------------------------------------------------------- numbers
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {

@@ -194,7 +194,8 @@ hipError_t launch_score_dot(const ScorePlan& p, hipStream_t s) {
 // lane-local up to one exchange between the two halves of the wave.
 // ========================================================================
 constexpr int kLtThreads = 256;
-constexpr int kLtTilesPerWave = 16;
+constexpr int kLtStages = 4;        // tiles in flight per wave
+constexpr int kLtTilesPerWave = 16; // a multiple of kLtStages
 constexpr int kLtTokensPerWG = (kLtThreads / kWave) * kLtTilesPerWave * 32;
 
 __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
@@ -207,6 +208,12 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
   r[4] = a2[0]; r[5] = a2[1]; r[6] = a3[0]; r[7] = a3[1];
   return r;
 }
+
+// One 32-token tile of a wave: 4 x 16-byte key loads and the token scale.
+struct LtTile {
+  uint4 k[4];
+  float sc;
+};
 
 template <int H>
 __global__ __launch_bounds__(kLtThreads) void score_lightning_kernel(
@@ -247,33 +254,27 @@ __global__ __launch_bounds__(kLtThreads) void score_lightning_kernel(
   const uint8_t* kb = (const uint8_t*)a.keys + (int64_t)b * a.k_stride_b;
   const float* ksb = a.k_scale + (int64_t)b * a.ks_stride_b;
   float* srow = scores + (int64_t)b * n_units;
-  const int t0 = blockIdx.x * kLtTokensPerWG + wid * 32;
   constexpr int kStride = (kLtThreads / kWave) * 32;
+  const int t0 = blockIdx.x * kLtTokensPerWG + wid * 32;
+  // tiles of this wave that hold at least one token
+  const int ntiles = t0 < n ? min(kLtTilesPerWave, (n - t0 + kStride - 1) / kStride) : 0;
 
-  auto load_tile = [&](int tile_base, uint4* raw) {
-    int t = tile_base + col;
+  auto issue = [&](LtTile& tl, int it) {
+    int t = t0 + it * kStride + col;
     t = t < n ? t : n - 1;
     const uint4* p = (const uint4*)(kb + (int64_t)t * a.k_stride_t + 64 * half);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) raw[i] = p[i];
+    for (int i = 0; i < 4; ++i) tl.k[i] = p[i];
+    tl.sc = ksb[t];
   };
 
-  uint4 cur[4], nxt[4];
-  if (t0 < n) load_tile(t0, cur);
-  for (int it = 0; it < kLtTilesPerWave; ++it) {
-    const int tb = t0 + it * kStride;
-    if (tb >= n) break;
-    const int tn = tb + kStride;
-    if (it + 1 < kLtTilesPerWave && tn < n) load_tile(tn, nxt);
-    const int t = tb + col;
-    const float sc = ksb[t < n ? t : n - 1];
-
+  auto consume = [&](const LtTile& tl, int it) {
     f32x16 acc[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[mt][e] = 0.f;
-    const uint32_t* w = (const uint32_t*)cur;
+    const uint32_t* w = (const uint32_t*)tl.k;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       bf16x8 kv = fp8x8_to_bf16(w[2 * s], w[2 * s + 1]);
@@ -289,14 +290,34 @@ __global__ __launch_bounds__(kLtThreads) void score_lightning_kernel(
     // lanes l and l^32 hold the two halves of the heads of the same token
     float other = swap_halves(sum);
     float total = half ? other + sum : sum + other;
-    float s_t = sc * total;
+    const int t = t0 + it * kStride + col;
+    float s_t = tl.sc * total;
     if (t >= valid) s_t = -__builtin_huge_valf();
     if (half == 0 && t < n) {
       srow[t] = s_t;
       if (hist && t < valid) lh.add(s_t);
     }
+  };
+
+  // kLtStages tiles in flight: tile it+kLtStages is issued into the buffer
+  // that tile it has just released.  A wave whose tiles are all full runs
+  // the fully unrolled loop, where every buffer index and every issue
+  // decision is a compile-time constant, so each tile waits for its own
+  // loads only.  The ragged last wave of a request takes the guarded loop.
+  LtTile buf[kLtStages];
+  if (ntiles == kLtTilesPerWave && t0 + (kLtTilesPerWave - 1) * kStride + 32 <= n) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) cur[i] = nxt[i];
+    for (int s = 0; s < kLtStages; ++s) issue(buf[s], s);
+#pragma unroll
+    for (int it = 0; it < kLtTilesPerWave; ++it) {
+      consume(buf[it % kLtStages], it);
+      if (it + kLtStages < kLtTilesPerWave) issue(buf[it % kLtStages], it + kLtStages);
+    }
+  } else {
+    for (int it = 0; it < ntiles; ++it) {
+      issue(buf[0], it);
+      consume(buf[0], it);
+    }
   }
   if (hist) {
     __syncthreads();
