@@ -62,7 +62,7 @@ IndexLayout index_layout(const sparse_index_args& a, bool with_scores) {
   auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
   const size_t cells = (size_t)L.rows * L.n_units;
   L.scores = with_scores ? take(cells * 4) : 0;
-  L.hist = take((size_t)L.rows * sd::kHistBins * 4);
+  L.hist = take((size_t)L.rows * sd::kHistStride * 4);
   L.cand_key = take(cells * 4);
   L.cand_idx = take(cells * 4);
   L.chunk_cnt = take((size_t)L.rows * std::max(L.n_chunks, 1) * 4);
@@ -249,9 +249,10 @@ int run_topk(const sd::TopkPlan& p, bool hist_ready, hipStream_t s) {
     return SPARSE_OK;
   }
   if (!hist_ready) {
-    HIPCHECK(sd::launch_zero_u32(p.hist, (int64_t)p.rows * sd::kHistBins, s));
+    HIPCHECK(sd::launch_zero_u32(p.hist, (int64_t)p.rows * sd::kHistStride, s));
     HIPCHECK(sd::launch_topk_hist(p, s));
   }
+  HIPCHECK(sd::launch_topk_bin(p, s));
   HIPCHECK(sd::launch_topk_filter(p, s));
   HIPCHECK(sd::launch_topk_select(p, s));
   return SPARSE_OK;
@@ -454,7 +455,7 @@ int sparse_decode_step(const sparse_index_args* ia, const sparse_attn_args* aa, 
   sd::TopkPlan tp = make_topk_plan(L, w, scores, L.n_units, ia->seq_lens, L.rows_per_b,
                                    unit, k, topk_out, nullptr);
   if (ia->n > 0) {
-    HIPCHECK(sd::launch_zero_u32(tp.hist, (int64_t)tp.rows * sd::kHistBins, s));
+    HIPCHECK(sd::launch_zero_u32(tp.hist, (int64_t)tp.rows * sd::kHistStride, s));
     rc = run_scores(*ia, L, w, scores, tp.hist, s);
     if (rc) return rc;
   }

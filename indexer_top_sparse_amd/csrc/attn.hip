@@ -257,37 +257,47 @@ __global__ __launch_bounds__(64 * NW) void attn_bf16_kernel(AttnPlan p) {
     }
   }
 
-  // ---- tile gather: kNch 16-byte chunks per thread, all loads unconditional
+  // ---- tile gather: kNch 16-byte chunks per thread, all loads unconditional.
+  // Chunk i of this thread is row crow[i] of the tile at byte offset
+  // coff[i] of that row's K (or, past the K chunks, V) data.
+  int crow[C::kNch];
+  int64_t coff[C::kNch];
+  int lofs[C::kNch];
+#pragma unroll
+  for (int i = 0; i < C::kNch; ++i) {
+    const int q = tid + i * C::kNT;
+    const int qc = q < C::kChunks ? q : C::kChunks - 1;
+    const bool isv = qc >= kTT * C::kCprK;
+    const int qq = isv ? qc - kTT * C::kCprK : qc;
+    const int cpr = isv ? C::kCprV : C::kCprK;
+    crow[i] = qq / cpr;
+    const int cc = qq % cpr;
+    coff[i] = (isv ? vdelta : 0) + 16 * cc;
+    // LDS destination: element offset in ks_s, or in vs_s with bit 30 set;
+    // -1 for the idle slots of the last round
+    lofs[i] = q < C::kChunks
+                  ? (isv ? (1 << 30) | (crow[i] * C::kRowV + 8 * cc) : crow[i] * C::kRowK + 8 * cc)
+                  : -1;
+  }
   auto gather = [&](u32x4 (&pre)[C::kNch], int tile) __attribute__((always_inline)) {
+    uint64_t w[C::kNch];
 #pragma unroll
     for (int i = 0; i < C::kNch; ++i) {
-      const int q = tid + i * C::kNT;
-      const int qc = q < C::kChunks ? q : C::kChunks - 1;
-      const bool isv = qc >= kTT * C::kCprK;
-      const int qq = isv ? qc - kTT * C::kCprK : qc;
-      const int cpr = isv ? C::kCprV : C::kCprK;
-      const int row = qq / cpr;
-      const int cc = qq % cpr;
-      const int it = tile * kTT + row;
-      const uint64_t w = it < cnt ? rowp_s[it] : dummy;
-      const char* base = (const char*)(w & ~15ull) + (isv ? vdelta : 0);
-      pre[i] = *(gptr<const u32x4>)(base + 16 * cc);
+      const int it = tile * kTT + crow[i];
+      w[i] = it < cnt ? rowp_s[it] : dummy;
     }
+#pragma unroll
+    for (int i = 0; i < C::kNch; ++i)
+      pre[i] = *(gptr<const u32x4>)((const char*)(w[i] & ~15ull) + coff[i]);
   };
   auto commit = [&](const u32x4 (&pre)[C::kNch]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < C::kNch; ++i) {
-      const int q = tid + i * C::kNT;
-      if (q < C::kChunks) {
-        const bool isv = q >= kTT * C::kCprK;
-        const int qq = isv ? q - kTT * C::kCprK : q;
-        const int cpr = isv ? C::kCprV : C::kCprK;
-        const int row = qq / cpr;
-        const int cc = qq % cpr;
-        uint16_t* dst = isv ? vs_s + row * C::kRowV : ks_s + row * C::kRowK;
-        *(u32x4*)(dst + 8 * cc) = pre[i];
+    for (int i = 0; i < C::kNch; ++i)
+      if (lofs[i] >= 0) {
+        uint16_t* dst = (lofs[i] & (1 << 30)) ? vs_s + (lofs[i] & ((1 << 30) - 1))
+                                               : ks_s + lofs[i];
+        *(u32x4*)dst = pre[i];
       }
-    }
   };
 
   // ---- softmax row state (replicated across the kTPR threads of a row)
@@ -311,11 +321,13 @@ __global__ __launch_bounds__(64 * NW) void attn_bf16_kernel(AttnPlan p) {
       f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
       const uint16_t* kr = ks_s + (16 * qnt + (lane & 15)) * C::kRowK +
                            32 * (kpart * C::kKSW) + 8 * (lane >> 4);
+      bf16x8 kv[C::kKSW];
+#pragma unroll
+      for (int s = 0; s < C::kKSW; ++s) kv[s] = *(const bf16x8*)(kr + 32 * s);
 #pragma unroll
       for (int s = 0; s < C::kKSW; ++s) {
-        bf16x8 kv = *(const bf16x8*)(kr + 32 * s);
-        if (s & 1) acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], kv, acc1, 0, 0, 0);
-        else acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], kv, acc0, 0, 0, 0);
+        if (s & 1) acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], kv[s], acc1, 0, 0, 0);
+        else acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], kv[s], acc0, 0, 0, 0);
       }
       const int colq = 16 * qnt + (lane & 15);
       float* sp = s_s + kpart * HG * kTT;
@@ -330,21 +342,27 @@ __global__ __launch_bounds__(64 * NW) void attn_bf16_kernel(AttnPlan p) {
     // ---- online softmax over the tile
     {
       float sv[C::kEPT];
-      float tmax = -__builtin_huge_valf();
+      float sp[C::kKSplit][C::kEPT];
+      uint64_t rw[C::kEPT];
 #pragma unroll
       for (int e = 0; e < C::kEPT; ++e) {
         const int col = ssub * C::kEPT + e;
+        const int it = tile * kTT + col;
+        rw[e] = it < cnt ? rowp_s[it] : 1ull;
+#pragma unroll
+        for (int kp = 0; kp < C::kKSplit; ++kp) sp[kp][e] = s_s[(kp * HG + srow) * kTT + col];
+      }
+      float tmax = -__builtin_huge_valf();
+#pragma unroll
+      for (int e = 0; e < C::kEPT; ++e) {
         float v = 0.f;
 #pragma unroll
-        for (int kp = 0; kp < C::kKSplit; ++kp) v += s_s[(kp * HG + srow) * kTT + col];
-        const int it = tile * kTT + col;
-        const bool ok = it < cnt && !(rowp_s[it] & 1ull);
-        sv[e] = ok ? v * A.sm_scale : -__builtin_huge_valf();
+        for (int kp = 0; kp < C::kKSplit; ++kp) v += sp[kp][e];
+        sv[e] = (rw[e] & 1ull) ? -__builtin_huge_valf() : v * A.sm_scale;
         tmax = fmaxf(tmax, sv[e]);
       }
-#pragma unroll
-      for (int off = C::kTPR / 2; off >= 1; off >>= 1)
-        tmax = fmaxf(tmax, __shfl_xor(tmax, off, 64));
+      static_assert(C::kTPR == 16, "softmax rows are 16-lane DPP rows");
+      tmax = row16_max(tmax);
       const float m_new = fmaxf(m_run, tmax);
       const bool none = (m_new == -__builtin_huge_valf());
       const float alpha = none ? 1.f : __expf(m_run - m_new);
@@ -356,8 +374,7 @@ __global__ __launch_bounds__(64 * NW) void attn_bf16_kernel(AttnPlan p) {
         psum += (float)pb;
         p_s[srow * (kTT + 8) + ssub * C::kEPT + e] = __builtin_bit_cast(uint16_t, pb);
       }
-#pragma unroll
-      for (int off = C::kTPR / 2; off >= 1; off >>= 1) psum += __shfl_xor(psum, off, 64);
+      psum = row16_sum(psum);
       l_run = alpha * l_run + psum;
       m_run = m_new;
       if (ssub == 0) alpha_s[srow] = alpha;
@@ -366,14 +383,11 @@ __global__ __launch_bounds__(64 * NW) void attn_bf16_kernel(AttnPlan p) {
 
     // ---- O = alpha * O + P V  (wave: all heads x kWC columns)
     {
+      float al[C::kMT][4];
 #pragma unroll
       for (int mt = 0; mt < C::kMT; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float al = alpha_s[16 * mt + 4 * (lane >> 4) + i];
-#pragma unroll
-          for (int nt = 0; nt < C::kCPL; ++nt) o[mt][nt][i] *= al;
-        }
+        for (int i = 0; i < 4; ++i) al[mt][i] = alpha_s[16 * mt + 4 * (lane >> 4) + i];
       bf16x8 pa[C::kMT];
 #pragma unroll
       for (int mt = 0; mt < C::kMT; ++mt)
@@ -396,6 +410,12 @@ __global__ __launch_bounds__(64 * NW) void attn_bf16_kernel(AttnPlan p) {
           raw[i][0] = *(const uint32_t*)vp;
         }
       }
+#pragma unroll
+      for (int mt = 0; mt < C::kMT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < C::kCPL; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[mt][nt][i] *= al[mt][i];
 #pragma unroll
       for (int nt = 0; nt < C::kCPL; ++nt) {
         const uint32_t sel = (nt & 1) ? 0x07060302u : 0x05040100u;

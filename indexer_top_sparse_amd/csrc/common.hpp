@@ -18,6 +18,14 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 
+constexpr int kTopkChunk = 4096;
+constexpr int kHistBins = 4096;
+// A histogram row: 4096 bins, then the boundary bin b* that holds the
+// k-th largest key and the count of units in higher bins.
+constexpr int kHistStride = kHistBins + 4;
+constexpr int kHistBstar = kHistBins;
+constexpr int kHistAbove = kHistBins + 1;
+
 // Pointer into the global address space: loads through it compile to
 // global_load (vector memory counter only) rather than flat_load.
 template <typename T>
@@ -46,6 +54,27 @@ __device__ __forceinline__ float swap_halves(float v) {
                                             __float_as_uint(v), false, false);
   uint32_t o = (threadIdx.x & 32) ? r[0] : r[1];
   return __uint_as_float(o);
+}
+
+// Reductions over each row of 16 lanes (DPP row rotates and quad perms; no
+// LDS round trip).  Every lane of the row receives the result.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, dpp_f<0x128>(x));  // row_ror:8
+  x = fmaxf(x, dpp_f<0x124>(x));  // row_ror:4
+  x = fmaxf(x, dpp_f<0x4E>(x));   // quad_perm [2,3,0,1]
+  x = fmaxf(x, dpp_f<0xB1>(x));   // quad_perm [1,0,3,2]
+  return x;
+}
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp_f<0x128>(x);
+  x += dpp_f<0x124>(x);
+  x += dpp_f<0x4E>(x);
+  x += dpp_f<0xB1>(x);
+  return x;
 }
 
 // ---------------------------------------------------------------- block scan
@@ -95,7 +124,7 @@ struct TopkPlan {
   const float* scores;
   const int32_t* valid;
   int32_t unit_div;  // valid units = ceil(valid / unit_div)
-  uint32_t* hist;    // [rows][4096]
+  uint32_t* hist;    // [rows][kHistStride]
   uint32_t* cand_key;  // [rows][n_units]
   int32_t* cand_idx;   // [rows][n_units]
   uint32_t* chunk_cnt; // [rows][n_chunks]
@@ -103,18 +132,17 @@ struct TopkPlan {
   float* val_out;
 };
 
-constexpr int kTopkChunk = 4096;
-constexpr int kHistBins = 4096;
 
 hipError_t launch_zero_u32(uint32_t* p, int64_t count, hipStream_t s);
 hipError_t launch_topk_hist(const TopkPlan& p, hipStream_t s);
+hipError_t launch_topk_bin(const TopkPlan& p, hipStream_t s);
 hipError_t launch_topk_filter(const TopkPlan& p, hipStream_t s);
 hipError_t launch_topk_select(const TopkPlan& p, hipStream_t s);
 
 struct ScorePlan {
   const sparse_index_args* a;
   float* scores;     // [B][R][n_units]
-  uint32_t* hist;    // [B*R][4096] (nullable: no fused histogram)
+  uint32_t* hist;    // [B*R][kHistStride] (nullable: no fused histogram)
   int n_units;
   int8_t* depth;     // BITPLANE: [B][Hkv][D]
   float* plane_w;    // BITPLANE: [B][Hkv][D][4] weight of each plane bit

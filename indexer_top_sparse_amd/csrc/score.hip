@@ -160,7 +160,8 @@ __global__ __launch_bounds__(kDotThreads) void score_dot_kernel(
   }
   if (hist) {
     __syncthreads();
-    lh.flush(hist + (int64_t)b * kHistBins, kDotThreads);
+    uint32_t* g = hist + (int64_t)b * kHistStride;
+    lh.flush(g, kDotThreads);
   }
 }
 
@@ -321,7 +322,8 @@ __global__ __launch_bounds__(kLtThreads) void score_lightning_kernel(
   }
   if (hist) {
     __syncthreads();
-    lh.flush(hist + (int64_t)b * kHistBins, kLtThreads);
+    uint32_t* g = hist + (int64_t)b * kHistStride;
+    lh.flush(g, kLtThreads);
   }
 }
 
@@ -488,7 +490,8 @@ __global__ __launch_bounds__(kBpThreads) void score_bitplane_kernel(
   }
   if (hist) {
     __syncthreads();
-    lh.flush(hist + ((int64_t)b * Hkv + h) * kHistBins, kBpThreads);
+    uint32_t* g = hist + ((int64_t)b * Hkv + h) * kHistStride;
+    lh.flush(g, kBpThreads);
   }
 }
 

@@ -9,12 +9,14 @@
 //   hist    rows x chunks workgroups: a 4096-bin histogram of the top 12 key
 //           bits of every valid unit (LDS, then global atomics).  The fused
 //           score kernels build the same histogram while they write scores.
-//   filter  rows x chunks workgroups: each finds the bin b* holding the k-th
-//           largest key from the histogram, then compacts, in index order,
-//           every unit whose bin is >= b* into its chunk's slice of a
-//           candidate buffer (keys and indices) and stores the chunk count.
-//   select  one workgroup per row: resolves the remaining 20 key bits over
-//           the few candidates of bin b* (two LDS histogram passes), which
+//   bin     one workgroup per row: the bin b* holding the k-th largest key,
+//           and the count of units above it.
+//   filter  rows x chunks workgroups: compacts, in index order, every unit
+//           whose bin is >= b* into its chunk's slice of a candidate buffer
+//           (keys and indices) and stores the chunk count.
+//   select  one workgroup per row: stages the candidates in LDS and resolves
+//           the remaining 20 key bits over those of bin b* (two histogram
+//           passes), which
 //           gives the exact k-th key T and how many units equal to T are
 //           needed, then writes the selection in index order with block
 //           prefix sums (ties to the lowest indices).
@@ -60,7 +62,7 @@ __global__ __launch_bounds__(256) void topk_hist_kernel(TopkPlan p) {
   for (int u = lo + threadIdx.x; u < hi; u += 256)
     atomicAdd(&h[score_key(row[u]) >> 20], 1u);
   __syncthreads();
-  uint32_t* g = p.hist + (int64_t)r * kHistBins;
+  uint32_t* g = p.hist + (int64_t)r * kHistStride;
   for (int i = threadIdx.x; i < kHistBins; i += 256)
     if (h[i]) atomicAdd(&g[i], h[i]);
 }
@@ -71,24 +73,22 @@ hipError_t launch_topk_hist(const TopkPlan& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Find the bin holding the k-th largest key.  NT threads; each thread owns
-// kHistBins/NT consecutive bins counted from the top.  Writes b* and the
-// number of units in higher bins to out[0], out[1].  k_eff >= 1.
+// Find, over `nbins` LDS bins counted from the top, the bin holding the
+// need-th largest key: out[0] = bin, out[1] = units in higher bins.
 template <int NT>
 __device__ void find_bin_from_top(const uint32_t* hist, int nbins, int need,
                                   int* scan_lds, int* out) {
-  constexpr int PER = kHistBins / NT;
-  const int per = nbins / NT;  // nbins is 4096 or 256 (and NT divides it)
-  (void)PER;
+  const int per = nbins / NT > 0 ? nbins / NT : 1;
   const int t = threadIdx.x;
-  // thread t covers bins [top - per*(t+1) + 1, top - per*t] (descending)
+  const bool owns = per * t < nbins;
   const int top = nbins - 1 - per * t;
   int local = 0;
-  for (int i = 0; i < per; ++i) local += (int)hist[top - i];
+  if (owns)
+    for (int i = 0; i < per; ++i) local += (int)hist[top - i];
   int total;
   int incl = block_inclusive_scan<NT>(local, scan_lds, &total);
   int excl = incl - local;
-  if (excl < need && incl >= need) {
+  if (owns && excl < need && incl >= need) {
     int cum = excl;
     for (int i = 0; i < per; ++i) {
       int b = top - i;
@@ -104,11 +104,37 @@ __device__ void find_bin_from_top(const uint32_t* hist, int nbins, int need,
   __syncthreads();
 }
 
+// --------------------------------------------------------------------- bin
+// One workgroup per row: the bin b* holding the k_eff-th largest key of the
+// complete histogram, and the number of units in higher bins, stored in the
+// row's tail for the filter and select kernels.
+constexpr int kBinThreads = 512;
+
+__global__ __launch_bounds__(kBinThreads) void topk_bin_kernel(TopkPlan p) {
+  __shared__ uint32_t hs[kHistBins];
+  __shared__ int scan_lds[kBinThreads / 64 + 1];
+  __shared__ int res[2];
+  const int r = blockIdx.x;
+  const int k_eff = min(p.k, row_valid_units(p, r));
+  uint32_t* g = p.hist + (int64_t)r * kHistStride;
+  for (int i = threadIdx.x; i < kHistBins; i += kBinThreads) hs[i] = g[i];
+  if (threadIdx.x == 0) { res[0] = 0; res[1] = 0; }
+  __syncthreads();
+  if (k_eff > 0) find_bin_from_top<kBinThreads>(hs, kHistBins, k_eff, scan_lds, res);
+  if (threadIdx.x == 0) {
+    g[kHistBstar] = (uint32_t)res[0];
+    g[kHistAbove] = (uint32_t)res[1];
+  }
+}
+
+hipError_t launch_topk_bin(const TopkPlan& p, hipStream_t s) {
+  topk_bin_kernel<<<p.rows, kBinThreads, 0, s>>>(p);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------------- filter
 __global__ __launch_bounds__(256) void topk_filter_kernel(TopkPlan p) {
-  __shared__ uint32_t hs[kHistBins];
   __shared__ int scan_lds[8];
-  __shared__ int res[2];
   const int r = blockIdx.y;
   const int c = blockIdx.x;
   const int v = row_valid_units(p, r);
@@ -118,13 +144,7 @@ __global__ __launch_bounds__(256) void topk_filter_kernel(TopkPlan p) {
     if (threadIdx.x == 0) *cnt = 0u;
     return;
   }
-  const uint32_t* g = p.hist + (int64_t)r * kHistBins;
-  for (int i = threadIdx.x; i < kHistBins; i += 256) hs[i] = g[i];
-  if (threadIdx.x == 0) { res[0] = 0; res[1] = 0; }
-  __syncthreads();
-  find_bin_from_top<256>(hs, kHistBins, k_eff, scan_lds, res);
-  const uint32_t bstar = (uint32_t)res[0];
-
+  const uint32_t bstar = p.hist[(int64_t)r * kHistStride + kHistBstar];
   const float* row = p.scores + (int64_t)r * p.row_stride;
   uint32_t* ck = p.cand_key + (int64_t)r * p.n_units + (int64_t)c * kTopkChunk;
   int32_t* ci = p.cand_idx + (int64_t)r * p.n_units + (int64_t)c * kTopkChunk;
@@ -168,6 +188,7 @@ hipError_t launch_topk_filter(const TopkPlan& p, hipStream_t s) {
 
 // ------------------------------------------------------------------- select
 constexpr int kSelThreads = 1024;
+constexpr int kSelCap = 12288;  // candidates staged in LDS (96 KB)
 
 __device__ __forceinline__ int find_chunk(const int* excl, int nchunks, int p) {
   // largest c with excl[c] <= p
@@ -180,6 +201,8 @@ __device__ __forceinline__ int find_chunk(const int* excl, int nchunks, int p) {
 }
 
 __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkPlan p) {
+  __shared__ uint32_t ckey_s[kSelCap];
+  __shared__ int32_t cidx_s[kSelCap];
   __shared__ uint32_t hs[kHistBins];
   __shared__ int excl[1025];
   __shared__ int scan_lds[kSelThreads / 64 + 1];
@@ -196,15 +219,9 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkPlan p) {
   }
   if (k_eff <= 0) return;
 
-  // level 1 (from the 12-bit histogram)
-  const uint32_t* g = p.hist + (int64_t)r * kHistBins;
-  for (int i = tid; i < kHistBins; i += kSelThreads) hs[i] = g[i];
-  if (tid == 0) { res[0] = 0; res[1] = 0; }
-  __syncthreads();
-  find_bin_from_top<kSelThreads>(hs, kHistBins, k_eff, scan_lds, res);
-  const uint32_t b1 = (uint32_t)res[0];
-  int above = res[1];
-  __syncthreads();
+  const uint32_t* g = p.hist + (int64_t)r * kHistStride;
+  const uint32_t b1 = g[kHistBstar];
+  int above = (int)g[kHistAbove];
 
   // chunk offsets
   const uint32_t* cc = p.chunk_cnt + (int64_t)r * p.n_chunks;
@@ -225,15 +242,25 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkPlan p) {
     int c = find_chunk(excl, nch, q);
     return (int64_t)c * kTopkChunk + (q - excl[c]);
   };
+  // stage the candidates (in index order) in LDS when they fit
+  const bool inlds = M <= kSelCap;
+  if (inlds) {
+    for (int q = tid; q < M; q += kSelThreads) {
+      const int64_t o = cand_off(q);
+      ckey_s[q] = ck[o];
+      cidx_s[q] = ci[o];
+    }
+  }
+  auto key_at = [&](int q) -> uint32_t { return inlds ? ckey_s[q] : ck[cand_off(q)]; };
+  auto idx_at = [&](int q) -> int32_t { return inlds ? cidx_s[q] : ci[cand_off(q)]; };
 
   // level 2: bits [19:8] of the keys in bin b1
   for (int i = tid; i < kHistBins; i += kSelThreads) hs[i] = 0u;
   __syncthreads();
   for (int q = tid; q < M; q += kSelThreads) {
-    uint32_t key = ck[cand_off(q)];
+    uint32_t key = key_at(q);
     if ((key >> 20) == b1) atomicAdd(&hs[(key >> 8) & 0xFFFu], 1u);
   }
-  __syncthreads();
   if (tid == 0) { res[0] = 0; res[1] = 0; }
   __syncthreads();
   find_bin_from_top<kSelThreads>(hs, kHistBins, k_eff - above, scan_lds, res);
@@ -246,54 +273,62 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkPlan p) {
   for (int i = tid; i < 256; i += kSelThreads) hs[i] = 0u;
   __syncthreads();
   for (int q = tid; q < M; q += kSelThreads) {
-    uint32_t key = ck[cand_off(q)];
+    uint32_t key = key_at(q);
     if ((key >> 8) == pre) atomicAdd(&hs[key & 0xFFu], 1u);
   }
-  __syncthreads();
   if (tid == 0) { res[0] = 0; res[1] = 0; }
   __syncthreads();
-  // 256 bins over 1024 threads: only the first 256 threads own bins
-  {
-    int local = tid < 256 ? (int)hs[255 - tid] : 0;
-    int total;
-    int incl = block_inclusive_scan<kSelThreads>(local, scan_lds, &total);
-    int ex = incl - local;
-    int need = k_eff - above;
-    if (tid < 256 && ex < need && incl >= need) {
-      res[0] = 255 - tid;
-      res[1] = ex;
-    }
-    __syncthreads();
-  }
-  const uint32_t T = (pre << 8) | (uint32_t)res[0];
+  find_bin_from_top<kSelThreads>(hs, 256, k_eff - above, scan_lds, res);
+  const uint32_t d3 = (uint32_t)res[0];
+  const uint32_t T = (pre << 8) | d3;
   const int count_gt = above + res[1];
   const int eq_need = k_eff - count_gt;
+  const int eq_total = (int)hs[d3];
   __syncthreads();
 
-  // final ordered pass
+  // final ordered pass, 4 consecutive candidates per thread per round
   int eq_carry = 0, take_carry = 0;
-  for (int base = 0; base < M; base += kSelThreads) {
-    int q = base + tid;
-    uint32_t key = 0;
-    int32_t idx = -1;
-    if (q < M) {
-      int64_t o = cand_off(q);
-      key = ck[o];
-      idx = ci[o];
+  const bool all_ties = (eq_total == eq_need);
+  for (int base = 0; base < M; base += 4 * kSelThreads) {
+    const int q0 = base + 4 * tid;
+    uint32_t key[4];
+    int gt[4], eq[4];
+    int n_eq = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = q0 + i;
+      key[i] = q < M ? key_at(q) : 0u;
+      gt[i] = (q < M) && key[i] > T;
+      eq[i] = (q < M) && key[i] == T;
+      n_eq += eq[i];
     }
-    int gt = (q < M) && key > T;
-    int eq = (q < M) && key == T;
+    int take[4];
+    if (all_ties) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) take[i] = gt[i] | eq[i];
+    } else {
+      int total;
+      int incl = block_inclusive_scan<kSelThreads>(n_eq, scan_lds, &total);
+      int rank = eq_carry + incl - n_eq;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        take[i] = gt[i] || (eq[i] && rank < eq_need);
+        rank += eq[i];
+      }
+      eq_carry += total;
+    }
+    const int n_take = take[0] + take[1] + take[2] + take[3];
     int total;
-    int eq_incl = block_inclusive_scan<kSelThreads>(eq, scan_lds, &total);
-    int eq_rank = eq_carry + eq_incl - eq;
-    eq_carry += total;
-    int take = gt || (eq && eq_rank < eq_need);
-    int t_incl = block_inclusive_scan<kSelThreads>(take, scan_lds, &total);
-    int pos = take_carry + t_incl - take;
+    int incl = block_inclusive_scan<kSelThreads>(n_take, scan_lds, &total);
+    int pos = take_carry + incl - n_take;
     take_carry += total;
-    if (take && pos < k_eff) {
-      oi[pos] = idx;
-      if (ov) ov[pos] = key_score(key);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (take[i] && pos < k_eff) {
+        oi[pos] = idx_at(q0 + i);
+        if (ov) ov[pos] = key_score(key[i]);
+        ++pos;
+      }
     }
   }
 }
