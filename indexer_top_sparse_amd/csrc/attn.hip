@@ -202,9 +202,15 @@ __global__ __launch_bounds__(64 * NW) void attn_bf16_kernel(AttnPlan p) {
   __shared__ uint64_t rowp_s[kMaxSplitTok];
 
   const sparse_attn_args& A = p.a;
-  const int split = blockIdx.x;
-  const int grp = blockIdx.y;
-  const int b = blockIdx.z;
+  // XCD-aware order: workgroup i runs on XCD i % 8, and the head groups of
+  // one (request, split) read the same KV rows, so they get ids that differ
+  // by multiples of 8 and are dispatched back to back on one XCD (one L2).
+  const int ngrp = (A.n_kv_heads == 1) ? A.n_q_heads / HG : A.n_kv_heads;
+  const int unit = (int)(blockIdx.x % 8) + 8 * (int)(blockIdx.x / (8 * ngrp));
+  const int grp = (int)(blockIdx.x / 8) % ngrp;
+  if (unit >= p.splits * A.batch) return;
+  const int split = unit % p.splits;
+  const int b = unit / p.splits;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wid = tid >> 6;
@@ -498,11 +504,16 @@ __global__ __launch_bounds__(64 * NW) void attn_bf16_kernel(AttnPlan p) {
 
 hipError_t launch_attn_bf16(const AttnPlan& p, hipStream_t s) {
   const sparse_attn_args& a = p.a;
+  // 8 * groups * ceil(units / 8) workgroup ids (the kernel decodes them)
+  const int64_t units = (int64_t)p.splits * a.batch;
+  const int64_t rounds = (units + 7) / 8;
   if (a.d_qk == 576 && a.d_v == 512 && a.v_cache == nullptr && a.n_kv_heads == 1) {
-    dim3 grid(p.splits, a.n_q_heads / 32, a.batch);
+    const int groups = a.n_q_heads / 32;
+    dim3 grid((unsigned)(8 * groups * rounds), 1, 1);
     attn_bf16_kernel<576, 512, 32, true, 8><<<grid, 512, 0, s>>>(p);
   } else if (a.d_qk == 128 && a.d_v == 128 && a.v_cache != nullptr) {
-    dim3 grid(p.splits, a.n_kv_heads, a.batch);
+    const int groups = a.n_kv_heads;
+    dim3 grid((unsigned)(8 * groups * rounds), 1, 1);
     attn_bf16_kernel<128, 128, 16, false, 4><<<grid, 256, 0, s>>>(p);
   } else {
     return hipErrorInvalidValue;

@@ -187,8 +187,12 @@ hipError_t launch_score_dot(const ScorePlan& p, hipStream_t s) {
 // (scale_t > 0 factors out of the ReLU).  The q.K tile is dense, so it runs
 // on MFMA: v_mfma_f32_32x32x16_bf16 with A = q (32 heads x 16 dims), B = the
 // fp8 keys converted exactly to bf16 in registers (16 dims x 32 tokens).
-// Lane l of a wave owns token (l % 32) of a 32-token tile and dims
-// [64*(l/32), 64*(l/32)+64) of its 128-byte key: 4 x 16-byte loads.  The
+//
+// A wave streams 32-token tiles (32 x 128 B): four non-temporal loads in
+// which the 64 lanes read one contiguous KiB each, so every load instruction
+// is fully coalesced.  The tile then passes through a wave-private LDS slot
+// (16-byte chunks XOR-swizzled by row to spread the banks) into the MFMA
+// layout: lane l owns token l % 32 and dims [64*(l/32), 64*(l/32)+64).  The
 // K-dim order inside the MFMA is permuted the same way for q and k, which
 // leaves the dot products unchanged.  The accumulator of lane l holds heads
 // 32*mt + 8*jj + 4*(l/32) + ii for token l % 32, so the weighted ReLU sum is
@@ -196,8 +200,7 @@ hipError_t launch_score_dot(const ScorePlan& p, hipStream_t s) {
 // ========================================================================
 constexpr int kLtThreads = 256;
 constexpr int kLtStages = 4;        // tiles in flight per wave
-constexpr int kLtTilesPerWave = 16; // a multiple of kLtStages
-constexpr int kLtTokensPerWG = (kLtThreads / kWave) * kLtTilesPerWave * 32;
+constexpr int kLtStride = (kLtThreads / kWave) * 32;  // tokens between a wave's tiles
 
 __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
   bf16x2 a0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
@@ -212,16 +215,19 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
 
 // One 32-token tile of a wave: 4 x 16-byte key loads and the token scale.
 struct LtTile {
-  uint4 k[4];
+  u32x4 k[4];
   float sc;
 };
 
-template <int H>
+// TPW: tiles per wave (a multiple of kLtStages); a workgroup covers
+// TPW * kLtStride tokens of one request.
+template <int H, int TPW>
 __global__ __launch_bounds__(kLtThreads) void score_lightning_kernel(
     sparse_index_args a, float* __restrict__ scores, uint32_t* hist,
     int n_units) {
   constexpr int MT = H / 32;  // 32-head MFMA row tiles
   __shared__ uint32_t hist_s[kHistBins];
+  __shared__ __attribute__((aligned(16))) u32x4 tile_s[kLtThreads / kWave][256];
   LdsHist lh{hist_s};
   const int b = blockIdx.y;
   const int lane = threadIdx.x & 63;
@@ -255,18 +261,40 @@ __global__ __launch_bounds__(kLtThreads) void score_lightning_kernel(
   const uint8_t* kb = (const uint8_t*)a.keys + (int64_t)b * a.k_stride_b;
   const float* ksb = a.k_scale + (int64_t)b * a.ks_stride_b;
   float* srow = scores + (int64_t)b * n_units;
-  constexpr int kStride = (kLtThreads / kWave) * 32;
-  const int t0 = blockIdx.x * kLtTokensPerWG + wid * 32;
+  constexpr int kStride = kLtStride;
+  const int t0 = blockIdx.x * (TPW * kLtStride) + wid * 32;
   // tiles of this wave that hold at least one token
-  const int ntiles = t0 < n ? min(kLtTilesPerWave, (n - t0 + kStride - 1) / kStride) : 0;
+  const int ntiles = t0 < n ? min(TPW, (n - t0 + kStride - 1) / kStride) : 0;
 
+  // The K-index is streamed exactly once per step: non-temporal loads keep
+  // it from displacing reusable lines in L2 and the last-level cache.
+  // Load j, lane l: row 8j + l/8 of the tile, 16-byte chunk l % 8.
+  u32x4* slot = tile_s[wid];
   auto issue = [&](LtTile& tl, int it) {
-    int t = t0 + it * kStride + col;
-    t = t < n ? t : n - 1;
-    const uint4* p = (const uint4*)(kb + (int64_t)t * a.k_stride_t + 64 * half);
+    const int tb = t0 + it * kStride;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) tl.k[i] = p[i];
-    tl.sc = ksb[t];
+    for (int j = 0; j < 4; ++j) {
+      int t = tb + 8 * j + (lane >> 3);
+      t = t < n ? t : n - 1;
+      tl.k[j] = __builtin_nontemporal_load(
+          (gptr<const u32x4>)(kb + (int64_t)t * a.k_stride_t + 16 * (lane & 7)));
+    }
+    int t = tb + col;
+    t = t < n ? t : n - 1;
+    tl.sc = __builtin_nontemporal_load((gptr<const float>)(ksb + t));
+  };
+  // Re-layout through LDS: chunk c of row r sits at r*8 + (c ^ (r & 7)).
+  auto transpose = [&](const LtTile& tl, u32x4 (&kk)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = 8 * j + (lane >> 3);
+      slot[r * 8 + ((lane & 7) ^ (r & 7))] = tl.k[j];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = col;
+      kk[i] = slot[r * 8 + ((4 * half + i) ^ (r & 7))];
+    }
   };
 
   auto consume = [&](const LtTile& tl, int it) {
@@ -275,7 +303,9 @@ __global__ __launch_bounds__(kLtThreads) void score_lightning_kernel(
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[mt][e] = 0.f;
-    const uint32_t* w = (const uint32_t*)tl.k;
+    u32x4 kk[4];
+    transpose(tl, kk);
+    const uint32_t* w = (const uint32_t*)kk;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       bf16x8 kv = fp8x8_to_bf16(w[2 * s], w[2 * s + 1]);
@@ -302,18 +332,24 @@ __global__ __launch_bounds__(kLtThreads) void score_lightning_kernel(
 
   // kLtStages tiles in flight: tile it+kLtStages is issued into the buffer
   // that tile it has just released.  A wave whose tiles are all full runs
-  // the fully unrolled loop, where every buffer index and every issue
-  // decision is a compile-time constant, so each tile waits for its own
-  // loads only.  The ragged last wave of a request takes the guarded loop.
+  // the loop below, unrolled by kLtStages so every buffer index is a
+  // compile-time constant and no load sits behind a branch; each tile then
+  // waits for its own loads only.  The ragged last wave of a request takes
+  // the guarded loop.
+  static_assert(TPW % kLtStages == 0, "whole stage groups");
   LtTile buf[kLtStages];
-  if (ntiles == kLtTilesPerWave && t0 + (kLtTilesPerWave - 1) * kStride + 32 <= n) {
+  if (ntiles == TPW && t0 + (TPW - 1) * kStride + 32 <= n) {
 #pragma unroll
     for (int s = 0; s < kLtStages; ++s) issue(buf[s], s);
+    for (int g = 0; g < TPW / kLtStages - 1; ++g) {
 #pragma unroll
-    for (int it = 0; it < kLtTilesPerWave; ++it) {
-      consume(buf[it % kLtStages], it);
-      if (it + kLtStages < kLtTilesPerWave) issue(buf[it % kLtStages], it + kLtStages);
+      for (int s = 0; s < kLtStages; ++s) {
+        consume(buf[s], g * kLtStages + s);
+        issue(buf[s], (g + 1) * kLtStages + s);
+      }
     }
+#pragma unroll
+    for (int s = 0; s < kLtStages; ++s) consume(buf[s], TPW - kLtStages + s);
   } else {
     for (int it = 0; it < ntiles; ++it) {
       issue(buf[0], it);
@@ -329,11 +365,20 @@ __global__ __launch_bounds__(kLtThreads) void score_lightning_kernel(
 
 hipError_t launch_score_lightning(const ScorePlan& p, hipStream_t s) {
   const sparse_index_args& a = *p.a;
-  dim3 grid((a.n + kLtTokensPerWG - 1) / kLtTokensPerWG, a.batch);
-  if (a.n_heads == 64)
-    score_lightning_kernel<64><<<grid, kLtThreads, 0, s>>>(a, p.scores, p.hist, p.n_units);
-  else
-    score_lightning_kernel<32><<<grid, kLtThreads, 0, s>>>(a, p.scores, p.hist, p.n_units);
+  // long spans per workgroup (fewer histogram clears and flushes) when the
+  // batch still gives at least two workgroups per compute unit
+  constexpr int kLong = 64, kShort = 16;
+  const int64_t long_wgs = (int64_t)a.batch * ((a.n + kLong * kLtStride - 1) / (kLong * kLtStride));
+  const bool use_long = long_wgs >= 512;
+  const int span = (use_long ? kLong : kShort) * kLtStride;
+  dim3 grid((a.n + span - 1) / span, a.batch);
+  if (a.n_heads == 64) {
+    if (use_long) score_lightning_kernel<64, kLong><<<grid, kLtThreads, 0, s>>>(a, p.scores, p.hist, p.n_units);
+    else score_lightning_kernel<64, kShort><<<grid, kLtThreads, 0, s>>>(a, p.scores, p.hist, p.n_units);
+  } else {
+    if (use_long) score_lightning_kernel<32, kLong><<<grid, kLtThreads, 0, s>>>(a, p.scores, p.hist, p.n_units);
+    else score_lightning_kernel<32, kShort><<<grid, kLtThreads, 0, s>>>(a, p.scores, p.hist, p.n_units);
+  }
   return hipGetLastError();
 }
 
