@@ -143,7 +143,9 @@ def main() -> int:
     dev = "cuda"
     print(f"[bench] generating inputs for {w.name}", file=sys.stderr, flush=True)
     sets = []
-    for s in range(2):
+    # two input sets alternate; the hot-buffer workloads (whose K-index alone
+    # is far larger than the last-level cache) use one to bound pinned memory
+    for s in range(1 if w.hot else 2):
         ws = w.with_(seed=w.seed + 100 * s)
         inp = synth.make_inputs(ws, dev)
         hot = None
@@ -157,8 +159,9 @@ def main() -> int:
     stream = torch.cuda.current_stream()
 
     # warmup (eager), then capture one graph per input set
+    ns = len(sets)
     for i in range(max(args.warmup, 1)):
-        sets[i % 2][1].run()
+        sets[i % ns][1].run()
     torch.cuda.synchronize()
     graphs = []
     if not args.no_graph:
@@ -168,16 +171,16 @@ def main() -> int:
                 r.run()
             graphs.append(g)
         for i in range(max(args.warmup, 1)):
-            graphs[i % 2].replay()
+            graphs[i % ns].replay()
     torch.cuda.synchronize()
 
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     t0 = time.perf_counter()
     for i in range(args.steps):
         if graphs:
-            graphs[i % 2].replay()
+            graphs[i % ns].replay()
         else:
-            sets[i % 2][1].run()
+            sets[i % ns][1].run()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms = 1e3 * elapsed / args.steps
@@ -191,7 +194,7 @@ def main() -> int:
     torch.cuda.synchronize()
     ev0.record(stream)
     for i in range(reps):
-        sets[i % 2][1].index_scores()
+        sets[i % ns][1].index_scores()
     ev1.record(stream)
     torch.cuda.synchronize()
     score_ms = ev0.elapsed_time(ev1) / reps

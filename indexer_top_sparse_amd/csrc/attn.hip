@@ -161,6 +161,7 @@ hipError_t launch_attn_f32(const AttnPlan& p, hipStream_t s) {
 constexpr int kTT = 32;           // tokens per tile
 constexpr int kStages = 3;        // tiles in flight (register prefetch)
 constexpr int kMaxSplitTok = 2048;
+constexpr int kMlaHeads = 32;     // query heads per workgroup for latent rows
 
 template <int DQK, int DV, int HG, bool LATENT, int NW>
 struct AttnCfg {
@@ -181,6 +182,9 @@ struct AttnCfg {
   static constexpr int kCPL = kWC / 16;                 // PV columns per lane
   static constexpr int kTPR = kNT / HG;                 // softmax threads per row
   static constexpr int kEPT = kTT / kTPR;               // softmax entries per thread
+  // S rows padded so the four 16-lane groups of an MFMA result write
+  // disjoint bank ranges
+  static constexpr int kSRow = kTT + 4;
   static_assert(NW % kPairs == 0 && kKS % kKSplit == 0, "QK work split");
   static_assert(kCPL == 2 || kCPL == 4 || kCPL == 8, "PV strip width");
   static_assert(kTPR <= 64 && kEPT >= 1, "softmax split");
@@ -194,7 +198,7 @@ __global__ __launch_bounds__(64 * NW) void attn_bf16_kernel(AttnPlan p) {
   using C = AttnCfg<DQK, DV, HG, LATENT, NW>;
   __shared__ __attribute__((aligned(16))) uint16_t ks_s[kTT * C::kRowK];
   __shared__ __attribute__((aligned(16))) uint16_t vs_s[LATENT ? 8 : kTT * C::kRowV];
-  __shared__ float s_s[C::kKSplit * HG * kTT];
+  __shared__ float s_s[C::kKSplit * HG * C::kSRow];
   __shared__ __attribute__((aligned(16))) uint16_t p_s[HG * (kTT + 8)];
   __shared__ float alpha_s[HG];
   __shared__ float m_s[HG];
@@ -336,11 +340,11 @@ __global__ __launch_bounds__(64 * NW) void attn_bf16_kernel(AttnPlan p) {
         else acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], kv[s], acc0, 0, 0, 0);
       }
       const int colq = 16 * qnt + (lane & 15);
-      float* sp = s_s + kpart * HG * kTT;
+      float* sp = s_s + kpart * HG * C::kSRow;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * qmt + 4 * (lane >> 4) + i;
-        sp[r * kTT + colq] = acc0[i] + acc1[i];
+        sp[r * C::kSRow + colq] = acc0[i] + acc1[i];
       }
     }
     __syncthreads();
@@ -356,7 +360,7 @@ __global__ __launch_bounds__(64 * NW) void attn_bf16_kernel(AttnPlan p) {
         const int it = tile * kTT + col;
         rw[e] = it < cnt ? rowp_s[it] : 1ull;
 #pragma unroll
-        for (int kp = 0; kp < C::kKSplit; ++kp) sp[kp][e] = s_s[(kp * HG + srow) * kTT + col];
+        for (int kp = 0; kp < C::kKSplit; ++kp) sp[kp][e] = s_s[(kp * HG + srow) * C::kSRow + col];
       }
       float tmax = -__builtin_huge_valf();
 #pragma unroll
@@ -508,9 +512,9 @@ hipError_t launch_attn_bf16(const AttnPlan& p, hipStream_t s) {
   const int64_t units = (int64_t)p.splits * a.batch;
   const int64_t rounds = (units + 7) / 8;
   if (a.d_qk == 576 && a.d_v == 512 && a.v_cache == nullptr && a.n_kv_heads == 1) {
-    const int groups = a.n_q_heads / 32;
+    const int groups = a.n_q_heads / kMlaHeads;
     dim3 grid((unsigned)(8 * groups * rounds), 1, 1);
-    attn_bf16_kernel<576, 512, 32, true, 8><<<grid, 512, 0, s>>>(p);
+    attn_bf16_kernel<576, 512, kMlaHeads, true, 8><<<grid, 512, 0, s>>>(p);
   } else if (a.d_qk == 128 && a.d_v == 128 && a.v_cache != nullptr) {
     const int groups = a.n_kv_heads;
     dim3 grid((unsigned)(8 * groups * rounds), 1, 1);

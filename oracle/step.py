@@ -146,7 +146,8 @@ def gqa_attention(q: np.ndarray, K_raw: np.ndarray, V_raw: np.ndarray,
     return out, lse
 
 
-def block_step(arr: dict, p: dict, sel_in: np.ndarray | None = None) -> dict:
+def block_step(arr: dict, p: dict, sel_in: np.ndarray | None = None,
+               requests=None) -> dict:
     """Block-sparse decode over several layers that share one selection.
 
     Layer 0 scores tokens with the head-summed dot, takes the max over each
@@ -154,13 +155,15 @@ def block_step(arr: dict, p: dict, sel_in: np.ndarray | None = None) -> dict:
     that selection with its own q, K and V ("MiniMax-M3" PR, description
     and Correctness note).  arr["layers"] is a list of dicts (q, k_cache,
     v_cache).  If sel_in is given, no scoring is done and that selection is
-    used by every layer.
+    used by every layer.  `requests` limits the step to those requests
+    (their results are stacked in that order).
     """
     B = arr["q_idx"].shape[0]
+    reqs = list(range(B)) if requests is None else list(requests)
     blk = p["block"]
     n_units = (p["n"] + blk - 1) // blk
     scores, sels = [], []
-    for b in range(B):
+    for b in reqs:
         valid = _valid(p, b)
         if sel_in is None:
             q = O.decode_bf16(arr["q_idx"][b])
@@ -176,9 +179,9 @@ def block_step(arr: dict, p: dict, sel_in: np.ndarray | None = None) -> dict:
     layer_out = []
     for layer in arr["layers"]:
         outs, lses = [], []
-        for b in range(B):
+        for i, b in enumerate(reqs):
             valid = _valid(p, b)
-            toks = O.expand_selection(sels[b, 0], blk, valid)
+            toks = O.expand_selection(sels[i, 0], blk, valid)
             q = O.decode_bf16(layer["q"][b])
             D = q.shape[1]
             K, V = layer["k_cache"][b], layer["v_cache"][b]

@@ -133,9 +133,14 @@ def make_inputs(w: Workload, device="cpu") -> dict:
         inp["q"] = _randn((B, w.hq, w.d_qk), _gen(w, 4, dev), dev,
                           torch.bfloat16)
         if w.hot:
-            # full latent KV lives in host memory; hot buffer built later
-            inp["host_kv"] = _randn((B, n, w.d_qk), _gen(w, 5, "cpu"), "cpu",
-                                    torch.bfloat16)
+            # full latent KV lives in host memory (hot buffer built later);
+            # drawn on `device` per request and copied into pinned memory
+            pinned = dev.type == "cuda"
+            host = torch.empty((B, n, w.d_qk), dtype=torch.bfloat16, pin_memory=pinned)
+            g = _gen(w, 5, dev)
+            for b in range(B):
+                host[b].copy_(_randn((n, w.d_qk), g, dev, torch.bfloat16))
+            inp["host_kv"] = host
         elif w.page:
             n_pages = (n + w.page - 1) // w.page
             inp["kv_pool"] = _randn((B * n_pages, w.page, w.d_qk),
