@@ -88,7 +88,8 @@ int attn_splits(const sparse_attn_args& a, int k_tokens) {
     min_tok = 64;
     target = 256;
   } else if (a.d_qk == 576) {
-    groups = a.n_q_heads / 32;
+    // one 4-wave workgroup per compute unit, 64 heads each
+    groups = a.n_q_heads / 64;
     min_tok = 256;
     target = 256;
   } else {
@@ -115,7 +116,7 @@ AttnLayout attn_layout(const sparse_attn_args& a, int k_tokens, size_t base) {
   size_t off = base;
   auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
   if (L.splits > 1)
-    L.part = take((size_t)a.batch * a.n_q_heads * L.splits * (a.d_v + 2) * 4);
+    L.part = take((size_t)a.batch * a.n_q_heads * L.splits * (a.d_v + 4) * 4);
   if (a.hot_slot) L.staging = take((size_t)a.batch * k_tokens * a.d_qk * 2);
   L.end = off;
   return L;
@@ -184,10 +185,10 @@ int check_attn(const sparse_attn_args* a, int sel_heads, int k, int sel_unit) {
     CHECK(a->hot_slot == nullptr, SPARSE_EUNSUPPORTED, "hot buffer needs bf16 latent rows");
   } else if (a->dtype == SPARSE_BF16) {
     const bool mla = a->d_qk == 576 && a->d_v == 512 && a->v_cache == nullptr &&
-                     a->n_kv_heads == 1 && a->n_q_heads % 32 == 0;
+                     a->n_kv_heads == 1 && a->n_q_heads % 64 == 0;
     const bool gqa = a->d_qk == 128 && a->d_v == 128 && a->v_cache != nullptr && G <= 16;
     CHECK(mla || gqa, SPARSE_EUNSUPPORTED,
-          "bf16 attention shapes: latent 576/512 (1 KV head, Hq %% 32 == 0) or "
+          "bf16 attention shapes: latent 576/512 (1 KV head, Hq %% 64 == 0) or "
           "128/128 with <= 16 query heads per KV head");
   } else {
     return fail(SPARSE_EUNSUPPORTED, "attention dtype %d", a->dtype);

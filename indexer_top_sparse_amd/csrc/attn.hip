@@ -136,7 +136,7 @@ __global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(AttnPlan p) {
     if (p.splits == 1) {
       p.out[oh * A.d_v + d] = l > 0.f ? acc / l : 0.f;
     } else {
-      p.part[(oh * p.splits + split) * (A.d_v + 2) + d] = acc;
+      p.part[(oh * p.splits + split) * (A.d_v + 4) + d] = acc;
     }
   }
   if (tid == 0) {
@@ -144,7 +144,7 @@ __global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(AttnPlan p) {
     if (p.splits == 1) {
       if (p.lse) p.lse[oh] = l > 0.f ? m + __logf(l) : -__builtin_huge_valf();
     } else {
-      float* pp = p.part + (oh * p.splits + split) * (A.d_v + 2);
+      float* pp = p.part + (oh * p.splits + split) * (A.d_v + 4);
       pp[A.d_v] = m;
       pp[A.d_v + 1] = l;
     }
@@ -489,7 +489,7 @@ __global__ __launch_bounds__(64 * NW) void attn_bf16_kernel(AttnPlan p) {
       for (int nt = 0; nt < C::kCPL; ++nt) {
         const int col = wid * C::kWC + C::kCPL * (lane & 15) + nt;
         if (p.splits == 1) p.out[oh * DV + col] = o[mt][nt][i] * inv;
-        else p.part[(oh * p.splits + split) * (DV + 2) + col] = o[mt][nt][i];
+        else p.part[(oh * p.splits + split) * (DV + 4) + col] = o[mt][nt][i];
       }
     }
   }
@@ -499,9 +499,292 @@ __global__ __launch_bounds__(64 * NW) void attn_bf16_kernel(AttnPlan p) {
     if (p.splits == 1) {
       if (p.lse) p.lse[oh] = l > 0.f ? m + __logf(l) : -__builtin_huge_valf();
     } else {
-      float* pp = p.part + (oh * p.splits + split) * (DV + 2);
+      float* pp = p.part + (oh * p.splits + split) * (DV + 4);
       pp[DV] = m;
       pp[DV + 1] = l;
+    }
+  }
+}
+
+// ============================================================ latent (MLA)
+// Latent rows (d_qk 576, values = the first 512 dims of the same row), one
+// KV head, 64 query heads per workgroup in four 16-head blocks.  Two waves
+// share a head block: each computes half of the QK contraction (288 dims)
+// and owns half of the 512 output columns.
+//   S^T[32 tokens x 16 heads] = K_tile Q^T  (A = K rows from LDS, B = q in
+//       registers); the two partial S^T of a block are summed after one
+//       exchange through LDS, so both waves hold identical scores
+//   online softmax per head in registers (lane l holds head l % 16; the four
+//       lanes of a head combine with permlane swaps)
+//   O^T[256 x 16] += V^T P^T  (A = V column strips from LDS, B = the lane's
+//       own probabilities)
+// The token order of the P V contraction is permuted so that the eight
+// probabilities a lane already holds (tokens 4g..4g+3 and 16+4g..16+4g+3,
+// g = lane / 16) are exactly its B operand.  K tiles rotate through three
+// LDS buffers with one more tile in flight in registers.  Probabilities
+// are taken relative to a per-head reference max that moves (rescaling O and
+// the sum) only when a tile's max exceeds it by more than e^8.
+constexpr int kMlaWaves = 8;
+constexpr int kMlaHeadsWG = 64;
+constexpr int kMlaThreads = 64 * kMlaWaves;
+constexpr int kMlaRow = 576 + 8;                   // LDS row stride (elements)
+constexpr int kMlaChunks = kTT * 72;               // 16-byte chunks per tile
+constexpr int kMlaNch = (kMlaChunks + kMlaThreads - 1) / kMlaThreads;  // 5
+
+__device__ __forceinline__ float xlane16(float v) {  // value of lane l ^ 16
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v),
+                                            false, false);
+  return __uint_as_float((threadIdx.x & 16) ? r[0] : r[1]);
+}
+
+__global__ __launch_bounds__(kMlaThreads, 1) void attn_mla_kernel(AttnPlan p) {
+  __shared__ __attribute__((aligned(16))) uint16_t ks_s[3][kTT * kMlaRow];
+  __shared__ __attribute__((aligned(16))) f32x4 sx_s[2][kMlaWaves][2][64];  // partial S^T
+  __shared__ uint64_t rowp_s[kMaxSplitTok];
+  __shared__ uint32_t vmask_s[kMaxSplitTok / kTT];  // valid tokens of each tile
+
+  const sparse_attn_args& A = p.a;
+  const int ngrp = A.n_q_heads / kMlaHeadsWG;
+  const int unit = (int)(blockIdx.x % 8) + 8 * (int)(blockIdx.x / (8 * ngrp));
+  const int grp = (int)(blockIdx.x / 8) % ngrp;
+  if (unit >= p.splits * A.batch) return;
+  const int split = unit % p.splits;
+  const int b = unit / p.splits;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wid = tid >> 6;
+  const int hb = wid & 3;           // 16-head block
+  const int half = wid >> 2;        // QK dims [288 half, +288), columns [256 half, +256)
+  const int g = lane >> 4;
+  const int n = lane & 15;
+  const int head = grp * kMlaHeadsWG + hb * 16 + n;
+  const int32_t* selrow = p.sel + (int64_t)b * p.sel_heads * p.k;
+  const int valid = valid_tokens(A, b);
+  const int tps = (p.k_tokens + p.splits - 1) / p.splits;
+  const int j0 = split * tps;
+  const int j1 = min(j0 + tps, p.k_tokens);
+  const int cnt = max(0, j1 - j0);
+  const int ntiles = (cnt + kTT - 1) / kTT;
+  const int64_t stage_base = (int64_t)b * p.sel_heads * p.k_tokens;
+  RowAddr ra{A};
+
+  const uint64_t dummy =
+      ((uint64_t)(A.hot_slot ? (const char*)A.hot_kv + (int64_t)b * A.hot_stride_b * 2
+                             : (const char*)A.k_cache)) | 1ull;
+  for (int i = tid; i < cnt; i += kMlaThreads) {
+    const int j = j0 + i;
+    const int t = sel_token(selrow, j, p.sel_unit, valid);
+    rowp_s[i] = t >= 0 ? (uint64_t)ra.k_row(b, 0, t, stage_base + j, p.staging, 2) : dummy;
+  }
+  // per-tile validity bits (bit j: token j of the tile is a selected row)
+  for (int tt = wid; tt < ntiles; tt += kMlaWaves) {
+    const int i = tt * kTT + (lane & 31);
+    int ok = 0;
+    if (i < cnt) {
+      const int t = sel_token(selrow, j0 + i, p.sel_unit, valid);
+      ok = t >= 0;
+    }
+    const uint64_t bal = __builtin_amdgcn_ballot_w64(ok && lane < 32);
+    if (lane == 0) vmask_s[tt] = (uint32_t)bal;
+  }
+
+  // q as the B operand: B[k = dim 32(9 half + s) + 8g + e][n = head]
+  bf16x8 qb[9];
+  {
+    const uint16_t* qp = (const uint16_t*)A.q + (int64_t)b * A.q_stride_b +
+                         (int64_t)head * A.q_stride_h + 288 * half + 8 * g;
+#pragma unroll
+    for (int s = 0; s < 9; ++s) qb[s] = *(const bf16x8*)(qp + 32 * s);
+  }
+
+  // gather coordinates: chunk i of this thread is row crow[i], chunk ccol[i]
+  int crow[kMlaNch], ccol[kMlaNch];
+#pragma unroll
+  for (int i = 0; i < kMlaNch; ++i) {
+    const int q = tid + i * kMlaThreads;
+    const int qc = q < kMlaChunks ? q : kMlaChunks - 1;
+    crow[i] = qc / 72;
+    ccol[i] = q < kMlaChunks ? qc % 72 : -1;
+  }
+  __syncthreads();  // rowp_s ready
+
+  auto gather = [&](u32x4 (&pre)[kMlaNch], int tile) __attribute__((always_inline)) {
+    uint64_t w[kMlaNch];
+#pragma unroll
+    for (int i = 0; i < kMlaNch; ++i) {
+      const int it = tile * kTT + crow[i];
+      w[i] = it < cnt ? rowp_s[it] : dummy;
+    }
+#pragma unroll
+    for (int i = 0; i < kMlaNch; ++i) {
+      const int cc = ccol[i] < 0 ? 0 : ccol[i];
+      pre[i] = *(gptr<const u32x4>)((const char*)(w[i] & ~15ull) + 16 * cc);
+    }
+  };
+  auto commit = [&](const u32x4 (&pre)[kMlaNch], int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < kMlaNch; ++i)
+      if (ccol[i] >= 0) *(u32x4*)(&ks_s[buf][crow[i] * kMlaRow + 8 * ccol[i]]) = pre[i];
+  };
+
+  float m_run = -__builtin_huge_valf();
+  float l_run = 0.f;
+  // O^T accumulators: m-tile (c, j) holds columns 256 half + 128c + 8m + j,
+  // m = 4g + i
+  f32x4 o[2][8];
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      for (int e = 0; e < 4; ++e) o[c][j][e] = 0.f;
+
+  // phase 1 of a tile: this wave's partial S^T into LDS
+  auto qk_partial = [&](int buf, int sb) __attribute__((always_inline)) {
+    const uint16_t* kt = ks_s[buf];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+      const uint16_t* kr = kt + (16 * mt + n) * kMlaRow + 288 * half + 8 * g;
+#pragma unroll
+      for (int s = 0; s < 9; ++s) {
+        bf16x8 kv = *(const bf16x8*)(kr + 32 * s);
+        if (s & 1) a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qb[s], a1, 0, 0, 0);
+        else a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qb[s], a0, 0, 0, 0);
+      }
+      sx_s[sb][wid][mt][lane] = a0 + a1;
+      __builtin_amdgcn_sched_barrier(0);  // bound the live K fragments
+    }
+  };
+
+  // phase 2: full scores, softmax, P V
+  auto finish = [&](int tile, int buf, int sb) __attribute__((always_inline)) {
+    const uint16_t* kt = ks_s[buf];
+    const uint32_t vm = vmask_s[tile];
+    float sv[8];
+    float tmax = -__builtin_huge_valf();
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const f32x4 mine = sx_s[sb][wid][mt][lane];
+      const f32x4 other = sx_s[sb][wid ^ 4][mt][lane];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool ok = (vm >> (16 * mt + 4 * g + i)) & 1u;
+        // identical in both waves of the block: IEEE addition commutes
+        const float v = ok ? (mine[i] + other[i]) * A.sm_scale : -__builtin_huge_valf();
+        sv[4 * mt + i] = v;
+        tmax = fmaxf(tmax, v);
+      }
+    }
+    tmax = fmaxf(tmax, xlane16(tmax));
+    tmax = fmaxf(tmax, swap_halves(tmax));
+    constexpr float kSlack = 8.0f;
+    if (__builtin_amdgcn_ballot_w64(tmax > m_run + kSlack)) {
+      const float m_new = fmaxf(m_run, tmax);
+      const float alpha = (m_run == -__builtin_huge_valf()) ? 0.f : __expf(m_run - m_new);
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[c][j][e] *= alpha;
+      l_run *= alpha;
+      m_run = m_new;
+    }
+    const bool none = (m_run == -__builtin_huge_valf());
+    float psum = 0.f;
+    uint32_t pk[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float p0 = none ? 0.f : __expf(sv[2 * e] - m_run);
+      const float p1 = none ? 0.f : __expf(sv[2 * e + 1] - m_run);
+      const __bf16 b0 = (__bf16)p0, b1 = (__bf16)p1;
+      psum += (float)b0 + (float)b1;
+      pk[e] = (uint32_t)__builtin_bit_cast(uint16_t, b0) |
+              ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+    }
+    psum += xlane16(psum);
+    psum += swap_halves(psum);
+    l_run += psum;
+    // B operand of P V: k = 8g + e  <->  token (e < 4 ? 4g + e : 16 + 4g + e - 4)
+    const bf16x8 pb = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      // lane reads columns 256 half + 128c + 8n .. +7 of its eight tokens
+      uint32_t raw[8][4];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int tok = e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4);
+        const uint4 v = *(const uint4*)(kt + tok * kMlaRow + 256 * half + 128 * c + 8 * n);
+        raw[e][0] = v.x; raw[e][1] = v.y; raw[e][2] = v.z; raw[e][3] = v.w;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+        uint32_t d[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          d[e] = __builtin_amdgcn_perm(raw[2 * e + 1][j >> 1], raw[2 * e][j >> 1], sel);
+        const bf16x8 va = __builtin_bit_cast(bf16x8, make_uint4(d[0], d[1], d[2], d[3]));
+        o[c][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, o[c][j], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);  // bound the live V strips
+    }
+  };
+
+  // ---- pipeline, one barrier per tile.  In step t the workgroup finishes
+  // tile t (softmax, P V from LDS buffer t % 3 and partial scores t % 2),
+  // computes the partial scores of tile t+1 (buffer (t+1) % 3), writes tile
+  // t+2 from registers into buffer (t+2) % 3 and starts loading tile t+3.
+  // Tiles past the split are fully masked and only ever partially scored.
+  u32x4 pre[kMlaNch];
+  if (ntiles > 0) {
+    gather(pre, 0);
+    commit(pre, 0);
+    gather(pre, 1);
+    commit(pre, 1);
+    gather(pre, 2);
+    __syncthreads();
+    qk_partial(0, 0);
+    __syncthreads();
+    for (int t = 0; t < ntiles; ++t) {
+      commit(pre, (t + 2) % 3);
+      gather(pre, t + 3);
+      qk_partial((t + 1) % 3, (t + 1) & 1);
+      finish(t, t % 3, t & 1);
+      __syncthreads();
+    }
+  }
+
+  // ---- epilogue: lane holds O^T[col][head n], col = 256 half + 128c + 32g + 8i + j
+  const int64_t oh = (int64_t)b * A.n_q_heads + head;
+  if (p.splits == 1) {
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    float* op = p.out + oh * 512 + 256 * half;
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f32x4 lo, hi;
+        for (int j = 0; j < 4; ++j) { lo[j] = o[c][j][i] * inv; hi[j] = o[c][j + 4][i] * inv; }
+        *(f32x4*)(op + 128 * c + 32 * g + 8 * i) = lo;
+        *(f32x4*)(op + 128 * c + 32 * g + 8 * i + 4) = hi;
+      }
+    if (half == 0 && g == 0 && p.lse)
+      p.lse[oh] = l_run > 0.f ? m_run + __logf(l_run) : -__builtin_huge_valf();
+  } else {
+    float* pp = p.part + (oh * p.splits + split) * (512 + 4);
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f32x4 lo, hi;
+        for (int j = 0; j < 4; ++j) { lo[j] = o[c][j][i]; hi[j] = o[c][j + 4][i]; }
+        *(f32x4*)(pp + 256 * half + 128 * c + 32 * g + 8 * i) = lo;
+        *(f32x4*)(pp + 256 * half + 128 * c + 32 * g + 8 * i + 4) = hi;
+      }
+    if (half == 0 && g == 0) {
+      pp[512] = m_run;
+      pp[513] = l_run;
     }
   }
 }
@@ -512,9 +795,9 @@ hipError_t launch_attn_bf16(const AttnPlan& p, hipStream_t s) {
   const int64_t units = (int64_t)p.splits * a.batch;
   const int64_t rounds = (units + 7) / 8;
   if (a.d_qk == 576 && a.d_v == 512 && a.v_cache == nullptr && a.n_kv_heads == 1) {
-    const int groups = a.n_q_heads / kMlaHeads;
+    const int groups = a.n_q_heads / kMlaHeadsWG;
     dim3 grid((unsigned)(8 * groups * rounds), 1, 1);
-    attn_bf16_kernel<576, 512, kMlaHeads, true, 8><<<grid, 512, 0, s>>>(p);
+    attn_mla_kernel<<<grid, kMlaThreads, 0, s>>>(p);
   } else if (a.d_qk == 128 && a.d_v == 128 && a.v_cache != nullptr) {
     const int groups = a.n_kv_heads;
     dim3 grid((unsigned)(8 * groups * rounds), 1, 1);
@@ -528,35 +811,37 @@ hipError_t launch_attn_bf16(const AttnPlan& p, hipStream_t s) {
 // ================================================================ combine
 // Merge split partials of one (request, head): M = max m_s,
 // L = sum l_s exp(m_s - M), out = sum o_s exp(m_s - M) / L, lse = M + log L.
-// One thread per output element.
-__global__ __launch_bounds__(256) void attn_combine_kernel(AttnPlan p) {
+// One workgroup per (request, head); each thread merges four columns.
+__global__ __launch_bounds__(128) void attn_combine_kernel(AttnPlan p) {
   const sparse_attn_args& A = p.a;
   const int dv = A.d_v;
   const int S = p.splits;
-  const int64_t total = (int64_t)A.batch * A.n_q_heads * dv;
-  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= total) return;
-  const int64_t oh = e / dv;
-  const int d = (int)(e % dv);
-  const float* pp = p.part + oh * S * (dv + 2);
+  const int64_t oh = blockIdx.x;
+  const float* pp = p.part + oh * S * (dv + 4);
   float M = -__builtin_huge_valf();
-  for (int s = 0; s < S; ++s) M = fmaxf(M, pp[s * (dv + 2) + dv]);
-  float L = 0.f, acc = 0.f;
+  for (int s = 0; s < S; ++s) M = fmaxf(M, pp[s * (dv + 4) + dv]);
+  float L = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  const int c = 4 * threadIdx.x;
   for (int s = 0; s < S; ++s) {
-    const float l = pp[s * (dv + 2) + dv + 1];
+    const float* ps = pp + s * (dv + 4);
+    const float l = ps[dv + 1];
     if (l > 0.f) {
-      const float f = __expf(pp[s * (dv + 2) + dv] - M);
+      const float f = __expf(ps[dv] - M);
       L += l * f;
-      acc += pp[s * (dv + 2) + d] * f;
+      if (c < dv) {
+        const f32x4 v = *(const f32x4*)(ps + c);
+        acc += v * f;
+      }
     }
   }
-  p.out[e] = L > 0.f ? acc / L : 0.f;
-  if (d == 0 && p.lse) p.lse[oh] = L > 0.f ? M + __logf(L) : -__builtin_huge_valf();
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  if (c < dv) *(f32x4*)(p.out + oh * dv + c) = acc * inv;
+  if (threadIdx.x == 0 && p.lse) p.lse[oh] = L > 0.f ? M + __logf(L) : -__builtin_huge_valf();
 }
 
 hipError_t launch_attn_combine(const AttnPlan& p, hipStream_t s) {
-  const int64_t total = (int64_t)p.a.batch * p.a.n_q_heads * p.a.d_v;
-  attn_combine_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(p);
+  attn_combine_kernel<<<(unsigned)((int64_t)p.a.batch * p.a.n_q_heads), 128, 0, s>>>(p);
   return hipGetLastError();
 }
 

@@ -161,7 +161,8 @@ struct AttnPlan {
   float* out;
   float* lse;
   int splits;         // token splits per (request, head group)
-  float* part;        // [B][Hq][splits][d_v + 2] partials when splits > 1
+  float* part;        // [B][Hq][splits][d_v + 4] partials when splits > 1:
+                      // d_v unnormalised sums, then max, sum, 2 pad
   // hot buffer: staging of fetched rows [B][k_tokens][d_qk] bf16
   uint16_t* staging;
   int k_tokens;       // selected tokens per (request, sel row)

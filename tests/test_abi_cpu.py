@@ -148,7 +148,7 @@ def test_attention_validation_codes():
     assert L.sparse_gather_attn_decode(ctypes.byref(a), FAKE, 1, 16, 1, FAKE, None,
                                        FAKE, 1 << 30, None) == isa.SPARSE_EUNSUPPORTED
     a = _mla_attn()
-    a.n_q_heads = 80  # not a multiple of 32
+    a.n_q_heads = 96  # not a multiple of 64
     assert L.sparse_gather_attn_decode(ctypes.byref(a), FAKE, 1, 16, 1, FAKE, None,
                                        FAKE, 1 << 30, None) == isa.SPARSE_EUNSUPPORTED
     a = _mla_attn()
