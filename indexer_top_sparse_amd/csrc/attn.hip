@@ -527,6 +527,14 @@ __global__ __launch_bounds__(64 * NW) void attn_bf16_kernel(AttnPlan p) {
 constexpr int kMlaWaves = 8;
 constexpr int kMlaHeadsWG = 64;
 constexpr int kMlaThreads = 64 * kMlaWaves;
+// floats in one split record of a (request, 64-head group): 64 x 512 partial
+// outputs, then (m, l) per head
+constexpr int kMlaRec = kMlaHeadsWG * 512 + 2 * kMlaHeadsWG;
+
+// The latent layout the MLA kernel serves (the API validates the head count).
+__host__ __device__ inline bool mla_shape(const sparse_attn_args& a) {
+  return a.d_qk == 576 && a.d_v == 512 && a.v_cache == nullptr && a.n_kv_heads == 1;
+}
 constexpr int kMlaRow = 576 + 8;                   // LDS row stride (elements)
 constexpr int kMlaChunks = kTT * 72;               // 16-byte chunks per tile
 constexpr int kMlaNch = (kMlaChunks + kMlaThreads - 1) / kMlaThreads;  // 5
@@ -568,6 +576,16 @@ __global__ __launch_bounds__(kMlaThreads, 1) void attn_mla_kernel(AttnPlan p) {
   const int64_t stage_base = (int64_t)b * p.sel_heads * p.k_tokens;
   RowAddr ra{A};
 
+  // q as the B operand: B[k = dim 32(9 half + s) + 8g + e][n = head]; its
+  // loads are issued first and complete while the row table is resolved
+  bf16x8 qb[9];
+  {
+    const uint16_t* qp = (const uint16_t*)A.q + (int64_t)b * A.q_stride_b +
+                         (int64_t)head * A.q_stride_h + 288 * half + 8 * g;
+#pragma unroll
+    for (int s = 0; s < 9; ++s) qb[s] = *(const bf16x8*)(qp + 32 * s);
+  }
+
   const uint64_t dummy =
       ((uint64_t)(A.hot_slot ? (const char*)A.hot_kv + (int64_t)b * A.hot_stride_b * 2
                              : (const char*)A.k_cache)) | 1ull;
@@ -575,26 +593,6 @@ __global__ __launch_bounds__(kMlaThreads, 1) void attn_mla_kernel(AttnPlan p) {
     const int j = j0 + i;
     const int t = sel_token(selrow, j, p.sel_unit, valid);
     rowp_s[i] = t >= 0 ? (uint64_t)ra.k_row(b, 0, t, stage_base + j, p.staging, 2) : dummy;
-  }
-  // per-tile validity bits (bit j: token j of the tile is a selected row)
-  for (int tt = wid; tt < ntiles; tt += kMlaWaves) {
-    const int i = tt * kTT + (lane & 31);
-    int ok = 0;
-    if (i < cnt) {
-      const int t = sel_token(selrow, j0 + i, p.sel_unit, valid);
-      ok = t >= 0;
-    }
-    const uint64_t bal = __builtin_amdgcn_ballot_w64(ok && lane < 32);
-    if (lane == 0) vmask_s[tt] = (uint32_t)bal;
-  }
-
-  // q as the B operand: B[k = dim 32(9 half + s) + 8g + e][n = head]
-  bf16x8 qb[9];
-  {
-    const uint16_t* qp = (const uint16_t*)A.q + (int64_t)b * A.q_stride_b +
-                         (int64_t)head * A.q_stride_h + 288 * half + 8 * g;
-#pragma unroll
-    for (int s = 0; s < 9; ++s) qb[s] = *(const bf16x8*)(qp + 32 * s);
   }
 
   // gather coordinates: chunk i of this thread is row crow[i], chunk ccol[i]
@@ -607,6 +605,14 @@ __global__ __launch_bounds__(kMlaThreads, 1) void attn_mla_kernel(AttnPlan p) {
     ccol[i] = q < kMlaChunks ? qc % 72 : -1;
   }
   __syncthreads();  // rowp_s ready
+  // per-tile validity bits (bit j: token j of the tile is a selected row);
+  // read by the first finish after the prologue's barriers
+  for (int tt = wid; tt < ntiles; tt += kMlaWaves) {
+    const int i = tt * kTT + (lane & 31);
+    const bool ok = lane < 32 && i < cnt && !(rowp_s[i] & 1ull);
+    const uint64_t bal = __builtin_amdgcn_ballot_w64(ok);
+    if (lane == 0) vmask_s[tt] = (uint32_t)bal;
+  }
 
   auto gather = [&](u32x4 (&pre)[kMlaNch], int tile) __attribute__((always_inline)) {
     uint64_t w[kMlaNch];
@@ -738,10 +744,13 @@ __global__ __launch_bounds__(kMlaThreads, 1) void attn_mla_kernel(AttnPlan p) {
   // Tiles past the split are fully masked and only ever partially scored.
   u32x4 pre[kMlaNch];
   if (ntiles > 0) {
-    gather(pre, 0);
-    commit(pre, 0);
-    gather(pre, 1);
-    commit(pre, 1);
+    {
+      u32x4 pre1[kMlaNch];
+      gather(pre, 0);
+      gather(pre1, 1);
+      commit(pre, 0);
+      commit(pre1, 1);
+    }
     gather(pre, 2);
     __syncthreads();
     qk_partial(0, 0);
@@ -772,19 +781,23 @@ __global__ __launch_bounds__(kMlaThreads, 1) void attn_mla_kernel(AttnPlan p) {
     if (half == 0 && g == 0 && p.lse)
       p.lse[oh] = l_run > 0.f ? m_run + __logf(l_run) : -__builtin_huge_valf();
   } else {
-    float* pp = p.part + (oh * p.splits + split) * (512 + 4);
+    // record of (request, head group, split) in register order: slot
+    // ((wave * 2 + c) * 4 + i) * 2 + hl holds one f32x4 per lane, so that
+    // every store writes 1 KiB contiguously; then (m, l) per head
+    float* pp = p.part + (((int64_t)b * ngrp + grp) * p.splits + split) * kMlaRec;
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         f32x4 lo, hi;
         for (int j = 0; j < 4; ++j) { lo[j] = o[c][j][i]; hi[j] = o[c][j + 4][i]; }
-        *(f32x4*)(pp + 256 * half + 128 * c + 32 * g + 8 * i) = lo;
-        *(f32x4*)(pp + 256 * half + 128 * c + 32 * g + 8 * i + 4) = hi;
+        const int slot = ((wid * 2 + c) * 4 + i) * 2;
+        *(f32x4*)(pp + (slot * 64 + lane) * 4) = lo;
+        *(f32x4*)(pp + ((slot + 1) * 64 + lane) * 4) = hi;
       }
     if (half == 0 && g == 0) {
-      pp[512] = m_run;
-      pp[513] = l_run;
+      pp[kMlaHeadsWG * 512 + 2 * (hb * 16 + n)] = m_run;
+      pp[kMlaHeadsWG * 512 + 2 * (hb * 16 + n) + 1] = l_run;
     }
   }
 }
@@ -794,7 +807,7 @@ hipError_t launch_attn_bf16(const AttnPlan& p, hipStream_t s) {
   // 8 * groups * ceil(units / 8) workgroup ids (the kernel decodes them)
   const int64_t units = (int64_t)p.splits * a.batch;
   const int64_t rounds = (units + 7) / 8;
-  if (a.d_qk == 576 && a.d_v == 512 && a.v_cache == nullptr && a.n_kv_heads == 1) {
+  if (mla_shape(a)) {
     const int groups = a.n_q_heads / kMlaHeadsWG;
     dim3 grid((unsigned)(8 * groups * rounds), 1, 1);
     attn_mla_kernel<<<grid, kMlaThreads, 0, s>>>(p);
@@ -840,8 +853,53 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnPlan p) {
   if (threadIdx.x == 0 && p.lse) p.lse[oh] = L > 0.f ? M + __logf(L) : -__builtin_huge_valf();
 }
 
+// Latent records (register order of the attention kernel): one workgroup
+// per (request, head group, attention wave); thread (ci = c * 4 + i, lane)
+// merges the two slots of that wave's lane and writes 8 contiguous columns.
+__global__ __launch_bounds__(512) void attn_combine_mla_kernel(AttnPlan p) {
+  const sparse_attn_args& A = p.a;
+  const int ngrp = A.n_q_heads / kMlaHeadsWG;
+  const int wv = (int)(blockIdx.x % kMlaWaves);
+  const int64_t bg = blockIdx.x / kMlaWaves;  // request * ngrp + group
+  const int b = (int)(bg / ngrp), grp = (int)(bg % ngrp);
+  const int tid = threadIdx.x, lane = tid & 63, ci = tid >> 6;
+  const int c = ci >> 2, i = ci & 3;
+  const int hb = wv & 3, half = wv >> 2, g = lane >> 4, n = lane & 15;
+  const int hl = hb * 16 + n;
+  const int S = p.splits;
+  const float* base = p.part + bg * S * kMlaRec;
+  float M = -__builtin_huge_valf();
+  for (int sp = 0; sp < S; ++sp) M = fmaxf(M, base[(int64_t)sp * kMlaRec + kMlaHeadsWG * 512 + 2 * hl]);
+  float L = 0.f;
+  f32x4 lo = {0.f, 0.f, 0.f, 0.f}, hi = {0.f, 0.f, 0.f, 0.f};
+  const int slot = ((wv * 2 + c) * 4 + i) * 2;
+  for (int sp = 0; sp < S; ++sp) {
+    const float* ps = base + (int64_t)sp * kMlaRec;
+    const float l = ps[kMlaHeadsWG * 512 + 2 * hl + 1];
+    if (l > 0.f) {
+      const float f = __expf(ps[kMlaHeadsWG * 512 + 2 * hl] - M);
+      L += l * f;
+      lo += *(const f32x4*)(ps + (slot * 64 + lane) * 4) * f;
+      hi += *(const f32x4*)(ps + ((slot + 1) * 64 + lane) * 4) * f;
+    }
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  const int64_t oh = (int64_t)b * A.n_q_heads + grp * kMlaHeadsWG + hl;
+  float* op = p.out + oh * 512 + 256 * half + 128 * c + 32 * g + 8 * i;
+  *(f32x4*)op = lo * inv;
+  *(f32x4*)(op + 4) = hi * inv;
+  if (ci == 0 && half == 0 && g == 0 && p.lse)
+    p.lse[oh] = L > 0.f ? M + __logf(L) : -__builtin_huge_valf();
+}
+
 hipError_t launch_attn_combine(const AttnPlan& p, hipStream_t s) {
-  attn_combine_kernel<<<(unsigned)((int64_t)p.a.batch * p.a.n_q_heads), 128, 0, s>>>(p);
+  const sparse_attn_args& a = p.a;
+  if (a.dtype == SPARSE_BF16 && mla_shape(a)) {
+    const int64_t wgs = (int64_t)a.batch * (a.n_q_heads / kMlaHeadsWG) * kMlaWaves;
+    attn_combine_mla_kernel<<<(unsigned)wgs, 512, 0, s>>>(p);
+  } else {
+    attn_combine_kernel<<<(unsigned)((int64_t)a.batch * a.n_q_heads), 128, 0, s>>>(p);
+  }
   return hipGetLastError();
 }
 
