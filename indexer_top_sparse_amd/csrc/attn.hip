@@ -514,21 +514,23 @@ __global__ __launch_bounds__(64 * NW) void attn_bf16_kernel(AttnPlan p) {
 //   S^T[32 tokens x 16 heads] = K_tile Q^T  (A = K rows from LDS, B = q in
 //       registers); the two partial S^T of a block are summed after one
 //       exchange through LDS, so both waves hold identical scores
-//   online softmax per head in registers (lane l holds head l % 16; the four
-//       lanes of a head combine with permlane swaps)
-//   O^T[256 x 16] += V^T P^T  (A = V column strips from LDS, B = the lane's
-//       own probabilities)
+//   online softmax per head in registers, in the base-2 domain (scores are
+//       scaled by sm_scale * log2(e)); lane l holds head l % 16 and the four
+//       lanes of a head combine with permlane swaps
+//   O^T[256 x 16] += V^T P^T  (A = V^T read from the row-major tile with the
+//       LDS transpose load ds_read_b64_tr_b16, B = the lane's own
+//       probabilities)
 // The token order of the P V contraction is permuted so that the eight
 // probabilities a lane already holds (tokens 4g..4g+3 and 16+4g..16+4g+3,
 // g = lane / 16) are exactly its B operand.  K tiles rotate through three
 // LDS buffers with one more tile in flight in registers.  Probabilities
 // are taken relative to a per-head reference max that moves (rescaling O and
-// the sum) only when a tile's max exceeds it by more than e^8.
+// the sum) only when a tile's max exceeds it by more than 2^8.
 constexpr int kMlaWaves = 8;
 constexpr int kMlaHeadsWG = 64;
 constexpr int kMlaThreads = 64 * kMlaWaves;
 // floats in one split record of a (request, 64-head group): 64 x 512 partial
-// outputs, then (m, l) per head
+// outputs, then (m, l) per head (m in the base-2 domain)
 constexpr int kMlaRec = kMlaHeadsWG * 512 + 2 * kMlaHeadsWG;
 
 // The latent layout the MLA kernel serves (the API validates the head count).
@@ -538,6 +540,9 @@ __host__ __device__ inline bool mla_shape(const sparse_attn_args& a) {
 constexpr int kMlaRow = 576 + 8;                   // LDS row stride (elements)
 constexpr int kMlaChunks = kTT * 72;               // 16-byte chunks per tile
 constexpr int kMlaNch = (kMlaChunks + kMlaThreads - 1) / kMlaThreads;  // 5
+constexpr int kMlaPad = 3 * kTT;  // row-table entries past a split (prefetch)
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ __forceinline__ float xlane16(float v) {  // value of lane l ^ 16
   auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v),
@@ -545,10 +550,19 @@ __device__ __forceinline__ float xlane16(float v) {  // value of lane l ^ 16
   return __uint_as_float((threadIdx.x & 16) ? r[0] : r[1]);
 }
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+// LDS transpose load: within each 16-lane group, lane i receives element
+// i % 4 of the 8-byte pieces addressed by lanes i / 4, 4 + i / 4, 8 + i / 4
+// and 12 + i / 4 (in that order).
+__device__ __forceinline__ s16x4 lds_read_tr16(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(uint16_t*)p);
+}
+
 __global__ __launch_bounds__(kMlaThreads, 1) void attn_mla_kernel(AttnPlan p) {
   __shared__ __attribute__((aligned(16))) uint16_t ks_s[3][kTT * kMlaRow];
   __shared__ __attribute__((aligned(16))) f32x4 sx_s[2][kMlaWaves][2][64];  // partial S^T
-  __shared__ uint64_t rowp_s[kMaxSplitTok];
+  __shared__ uint64_t rowp_s[kMaxSplitTok + kMlaPad];
   __shared__ uint32_t vmask_s[kMaxSplitTok / kTT];  // valid tokens of each tile
 
   const sparse_attn_args& A = p.a;
@@ -586,63 +600,58 @@ __global__ __launch_bounds__(kMlaThreads, 1) void attn_mla_kernel(AttnPlan p) {
     for (int s = 0; s < 9; ++s) qb[s] = *(const bf16x8*)(qp + 32 * s);
   }
 
+  // Row table: the K row address of every split position (masked positions
+  // and the prefetch pad point at a finite dummy row, so every load in the
+  // pipeline is unconditional) and, per 32-token tile, the valid-token bits.
   const uint64_t dummy =
-      ((uint64_t)(A.hot_slot ? (const char*)A.hot_kv + (int64_t)b * A.hot_stride_b * 2
-                             : (const char*)A.k_cache)) | 1ull;
-  for (int i = tid; i < cnt; i += kMlaThreads) {
-    const int j = j0 + i;
-    const int t = sel_token(selrow, j, p.sel_unit, valid);
-    rowp_s[i] = t >= 0 ? (uint64_t)ra.k_row(b, 0, t, stage_base + j, p.staging, 2) : dummy;
+      (uint64_t)(A.hot_slot ? (const char*)A.hot_kv + (int64_t)b * A.hot_stride_b * 2
+                            : (const char*)A.k_cache);
+  for (int base = 0; base < cnt; base += kMlaThreads) {
+    const int i = base + tid;
+    int t = -1;
+    if (i < cnt) {
+      t = sel_token(selrow, j0 + i, p.sel_unit, valid);
+      rowp_s[i] = t >= 0 ? (uint64_t)ra.k_row(b, 0, t, stage_base + j0 + i, p.staging, 2)
+                         : dummy;
+    }
+    const uint64_t bal = __builtin_amdgcn_ballot_w64(t >= 0);
+    const int tile = (base >> 5) + 2 * wid;  // lanes 0..31: tile, 32..63: tile + 1
+    if (lane == 0 && tile < ntiles) vmask_s[tile] = (uint32_t)bal;
+    if (lane == 0 && tile + 1 < ntiles) vmask_s[tile + 1] = (uint32_t)(bal >> 32);
   }
+  for (int i = cnt + tid; i < (ntiles + 3) * kTT; i += kMlaThreads) rowp_s[i] = dummy;
 
-  // gather coordinates: chunk i of this thread is row crow[i], chunk ccol[i]
-  int crow[kMlaNch], ccol[kMlaNch];
+  // gather coordinates: chunk i of this thread is row crow[i], byte offset
+  // coff[i] of the row, LDS element offset lofs[i] (-1: no chunk)
+  int crow[kMlaNch], coff[kMlaNch], lofs[kMlaNch];
 #pragma unroll
   for (int i = 0; i < kMlaNch; ++i) {
     const int q = tid + i * kMlaThreads;
     const int qc = q < kMlaChunks ? q : kMlaChunks - 1;
     crow[i] = qc / 72;
-    ccol[i] = q < kMlaChunks ? qc % 72 : -1;
+    coff[i] = 16 * (qc % 72);
+    lofs[i] = q < kMlaChunks ? crow[i] * kMlaRow + 8 * (qc % 72) : -1;
   }
-  __syncthreads();  // rowp_s ready
-  // per-tile validity bits (bit j: token j of the tile is a selected row);
-  // read by the first finish after the prologue's barriers
-  for (int tt = wid; tt < ntiles; tt += kMlaWaves) {
-    const int i = tt * kTT + (lane & 31);
-    const bool ok = lane < 32 && i < cnt && !(rowp_s[i] & 1ull);
-    const uint64_t bal = __builtin_amdgcn_ballot_w64(ok);
-    if (lane == 0) vmask_s[tt] = (uint32_t)bal;
-  }
+  __syncthreads();  // row table ready
 
   auto gather = [&](u32x4 (&pre)[kMlaNch], int tile) __attribute__((always_inline)) {
-    uint64_t w[kMlaNch];
 #pragma unroll
-    for (int i = 0; i < kMlaNch; ++i) {
-      const int it = tile * kTT + crow[i];
-      w[i] = it < cnt ? rowp_s[it] : dummy;
-    }
-#pragma unroll
-    for (int i = 0; i < kMlaNch; ++i) {
-      const int cc = ccol[i] < 0 ? 0 : ccol[i];
-      pre[i] = *(gptr<const u32x4>)((const char*)(w[i] & ~15ull) + 16 * cc);
-    }
+    for (int i = 0; i < kMlaNch; ++i)
+      pre[i] = *(gptr<const u32x4>)((const char*)rowp_s[tile * kTT + crow[i]] + coff[i]);
   };
   auto commit = [&](const u32x4 (&pre)[kMlaNch], int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < kMlaNch; ++i)
-      if (ccol[i] >= 0) *(u32x4*)(&ks_s[buf][crow[i] * kMlaRow + 8 * ccol[i]]) = pre[i];
+      if (lofs[i] >= 0) *(u32x4*)(&ks_s[buf][lofs[i]]) = pre[i];
   };
 
-  float m_run = -__builtin_huge_valf();
+  const float qk_scale = A.sm_scale * kLog2e;
+  float m_run = -__builtin_huge_valf();  // base-2 reference max
   float l_run = 0.f;
-  // O^T accumulators: m-tile (c, j) holds columns 256 half + 128c + 8m + j,
-  // m = 4g + i
-  f32x4 o[2][8];
+  // O^T accumulators: m-tile mt holds columns 256 half + 16 mt + 4g + i
+  f32x4 o[16];
 #pragma unroll
-  for (int c = 0; c < 2; ++c)
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      for (int e = 0; e < 4; ++e) o[c][j][e] = 0.f;
+  for (int mt = 0; mt < 16; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // phase 1 of a tile: this wave's partial S^T into LDS
   auto qk_partial = [&](int buf, int sb) __attribute__((always_inline)) {
@@ -663,36 +672,35 @@ __global__ __launch_bounds__(kMlaThreads, 1) void attn_mla_kernel(AttnPlan p) {
   };
 
   // phase 2: full scores, softmax, P V
+  const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3F803F80u);
   auto finish = [&](int tile, int buf, int sb) __attribute__((always_inline)) {
     const uint16_t* kt = ks_s[buf];
-    const uint32_t vm = vmask_s[tile];
+    const uint32_t vm = __builtin_amdgcn_readfirstlane(vmask_s[tile]);
     float sv[8];
-    float tmax = -__builtin_huge_valf();
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       const f32x4 mine = sx_s[sb][wid][mt][lane];
       const f32x4 other = sx_s[sb][wid ^ 4][mt][lane];
+      // identical in both waves of the block: IEEE addition commutes
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bool ok = (vm >> (16 * mt + 4 * g + i)) & 1u;
-        // identical in both waves of the block: IEEE addition commutes
-        const float v = ok ? (mine[i] + other[i]) * A.sm_scale : -__builtin_huge_valf();
-        sv[4 * mt + i] = v;
-        tmax = fmaxf(tmax, v);
-      }
+      for (int i = 0; i < 4; ++i) sv[4 * mt + i] = (mine[i] + other[i]) * qk_scale;
     }
+    if (vm != 0xFFFFFFFFu) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (!((vm >> (16 * (e >> 2) + 4 * g + (e & 3))) & 1u)) sv[e] = -__builtin_huge_valf();
+    }
+    float tmax = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                       fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
     tmax = fmaxf(tmax, xlane16(tmax));
     tmax = fmaxf(tmax, swap_halves(tmax));
     constexpr float kSlack = 8.0f;
     if (__builtin_amdgcn_ballot_w64(tmax > m_run + kSlack)) {
       const float m_new = fmaxf(m_run, tmax);
-      const float alpha = (m_run == -__builtin_huge_valf()) ? 0.f : __expf(m_run - m_new);
+      const float alpha =
+          (m_run == -__builtin_huge_valf()) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) o[c][j][e] *= alpha;
+      for (int mt = 0; mt < 16; ++mt) o[mt] *= alpha;
       l_run *= alpha;
       m_run = m_new;
     }
@@ -701,39 +709,28 @@ __global__ __launch_bounds__(kMlaThreads, 1) void attn_mla_kernel(AttnPlan p) {
     uint32_t pk[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float p0 = none ? 0.f : __expf(sv[2 * e] - m_run);
-      const float p1 = none ? 0.f : __expf(sv[2 * e + 1] - m_run);
-      const __bf16 b0 = (__bf16)p0, b1 = (__bf16)p1;
-      psum += (float)b0 + (float)b1;
-      pk[e] = (uint32_t)__builtin_bit_cast(uint16_t, b0) |
-              ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+      const float p0 = none ? 0.f : __builtin_amdgcn_exp2f(sv[2 * e] - m_run);
+      const float p1 = none ? 0.f : __builtin_amdgcn_exp2f(sv[2 * e + 1] - m_run);
+      const bf16x2 pp = bf16x2{(__bf16)p0, (__bf16)p1};
+      psum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, psum, false);
+      pk[e] = __builtin_bit_cast(uint32_t, pp);
     }
     psum += xlane16(psum);
     psum += swap_halves(psum);
     l_run += psum;
     // B operand of P V: k = 8g + e  <->  token (e < 4 ? 4g + e : 16 + 4g + e - 4)
     const bf16x8 pb = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+    // A operand, m-tile mt: lane (g, n) needs column 256 half + 16 mt + n of
+    // those eight tokens; lane n of each group addresses token row n / 4 of
+    // the four and columns 4 (n % 4) .. +3
+    const uint16_t* vb = kt + (4 * g + (n >> 2)) * kMlaRow + 256 * half + 4 * (n & 3);
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      // lane reads columns 256 half + 128c + 8n .. +7 of its eight tokens
-      uint32_t raw[8][4];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int tok = e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4);
-        const uint4 v = *(const uint4*)(kt + tok * kMlaRow + 256 * half + 128 * c + 8 * n);
-        raw[e][0] = v.x; raw[e][1] = v.y; raw[e][2] = v.z; raw[e][3] = v.w;
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
-        uint32_t d[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          d[e] = __builtin_amdgcn_perm(raw[2 * e + 1][j >> 1], raw[2 * e][j >> 1], sel);
-        const bf16x8 va = __builtin_bit_cast(bf16x8, make_uint4(d[0], d[1], d[2], d[3]));
-        o[c][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, o[c][j], 0, 0, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);  // bound the live V strips
+    for (int mt = 0; mt < 16; ++mt) {
+      const s16x4 r0 = lds_read_tr16(vb + 16 * mt);
+      const s16x4 r1 = lds_read_tr16(vb + 16 * kMlaRow + 16 * mt);
+      const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7));
+      o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, o[mt], 0, 0, 0);
+      if ((mt & 7) == 7) __builtin_amdgcn_sched_barrier(0);  // bound the live V fragments
     }
   };
 
@@ -764,37 +761,22 @@ __global__ __launch_bounds__(kMlaThreads, 1) void attn_mla_kernel(AttnPlan p) {
     }
   }
 
-  // ---- epilogue: lane holds O^T[col][head n], col = 256 half + 128c + 32g + 8i + j
+  // ---- epilogue: lane holds O^T[col][head n], col = 256 half + 16 mt + 4g + i
   const int64_t oh = (int64_t)b * A.n_q_heads + head;
   if (p.splits == 1) {
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-    float* op = p.out + oh * 512 + 256 * half;
+    float* op = p.out + oh * 512 + 256 * half + 4 * g;
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f32x4 lo, hi;
-        for (int j = 0; j < 4; ++j) { lo[j] = o[c][j][i] * inv; hi[j] = o[c][j + 4][i] * inv; }
-        *(f32x4*)(op + 128 * c + 32 * g + 8 * i) = lo;
-        *(f32x4*)(op + 128 * c + 32 * g + 8 * i + 4) = hi;
-      }
+    for (int mt = 0; mt < 16; ++mt) *(f32x4*)(op + 16 * mt) = o[mt] * inv;
     if (half == 0 && g == 0 && p.lse)
-      p.lse[oh] = l_run > 0.f ? m_run + __logf(l_run) : -__builtin_huge_valf();
+      p.lse[oh] = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : -__builtin_huge_valf();
   } else {
     // record of (request, head group, split) in register order: slot
-    // ((wave * 2 + c) * 4 + i) * 2 + hl holds one f32x4 per lane, so that
-    // every store writes 1 KiB contiguously; then (m, l) per head
+    // wave * 16 + mt holds one f32x4 per lane, so that every store writes
+    // 1 KiB contiguously; then (m, l) per head
     float* pp = p.part + (((int64_t)b * ngrp + grp) * p.splits + split) * kMlaRec;
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f32x4 lo, hi;
-        for (int j = 0; j < 4; ++j) { lo[j] = o[c][j][i]; hi[j] = o[c][j + 4][i]; }
-        const int slot = ((wid * 2 + c) * 4 + i) * 2;
-        *(f32x4*)(pp + (slot * 64 + lane) * 4) = lo;
-        *(f32x4*)(pp + ((slot + 1) * 64 + lane) * 4) = hi;
-      }
+    for (int mt = 0; mt < 16; ++mt) *(f32x4*)(pp + ((wid * 16 + mt) * 64 + lane) * 4) = o[mt];
     if (half == 0 && g == 0) {
       pp[kMlaHeadsWG * 512 + 2 * (hb * 16 + n)] = m_run;
       pp[kMlaHeadsWG * 512 + 2 * (hb * 16 + n) + 1] = l_run;
@@ -853,43 +835,43 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnPlan p) {
   if (threadIdx.x == 0 && p.lse) p.lse[oh] = L > 0.f ? M + __logf(L) : -__builtin_huge_valf();
 }
 
-// Latent records (register order of the attention kernel): one workgroup
-// per (request, head group, attention wave); thread (ci = c * 4 + i, lane)
-// merges the two slots of that wave's lane and writes 8 contiguous columns.
+// Latent records (register order of the attention kernel, base-2 m): one
+// workgroup per (request, head group, attention wave); thread (q, lane)
+// merges slots 2q and 2q + 1 of that wave's lane.
 __global__ __launch_bounds__(512) void attn_combine_mla_kernel(AttnPlan p) {
   const sparse_attn_args& A = p.a;
   const int ngrp = A.n_q_heads / kMlaHeadsWG;
   const int wv = (int)(blockIdx.x % kMlaWaves);
   const int64_t bg = blockIdx.x / kMlaWaves;  // request * ngrp + group
   const int b = (int)(bg / ngrp), grp = (int)(bg % ngrp);
-  const int tid = threadIdx.x, lane = tid & 63, ci = tid >> 6;
-  const int c = ci >> 2, i = ci & 3;
+  const int tid = threadIdx.x, lane = tid & 63, q = tid >> 6;
   const int hb = wv & 3, half = wv >> 2, g = lane >> 4, n = lane & 15;
   const int hl = hb * 16 + n;
   const int S = p.splits;
   const float* base = p.part + bg * S * kMlaRec;
   float M = -__builtin_huge_valf();
-  for (int sp = 0; sp < S; ++sp) M = fmaxf(M, base[(int64_t)sp * kMlaRec + kMlaHeadsWG * 512 + 2 * hl]);
+  for (int sp = 0; sp < S; ++sp)
+    M = fmaxf(M, base[(int64_t)sp * kMlaRec + kMlaHeadsWG * 512 + 2 * hl]);
   float L = 0.f;
-  f32x4 lo = {0.f, 0.f, 0.f, 0.f}, hi = {0.f, 0.f, 0.f, 0.f};
-  const int slot = ((wv * 2 + c) * 4 + i) * 2;
+  f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+  const int slot = wv * 16 + 2 * q;
   for (int sp = 0; sp < S; ++sp) {
     const float* ps = base + (int64_t)sp * kMlaRec;
     const float l = ps[kMlaHeadsWG * 512 + 2 * hl + 1];
     if (l > 0.f) {
-      const float f = __expf(ps[kMlaHeadsWG * 512 + 2 * hl] - M);
+      const float f = __builtin_amdgcn_exp2f(ps[kMlaHeadsWG * 512 + 2 * hl] - M);
       L += l * f;
-      lo += *(const f32x4*)(ps + (slot * 64 + lane) * 4) * f;
-      hi += *(const f32x4*)(ps + ((slot + 1) * 64 + lane) * 4) * f;
+      a0 += *(const f32x4*)(ps + (slot * 64 + lane) * 4) * f;
+      a1 += *(const f32x4*)(ps + ((slot + 1) * 64 + lane) * 4) * f;
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
   const int64_t oh = (int64_t)b * A.n_q_heads + grp * kMlaHeadsWG + hl;
-  float* op = p.out + oh * 512 + 256 * half + 128 * c + 32 * g + 8 * i;
-  *(f32x4*)op = lo * inv;
-  *(f32x4*)(op + 4) = hi * inv;
-  if (ci == 0 && half == 0 && g == 0 && p.lse)
-    p.lse[oh] = L > 0.f ? M + __logf(L) : -__builtin_huge_valf();
+  float* op = p.out + oh * 512 + 256 * half + 32 * q + 4 * g;
+  *(f32x4*)op = a0 * inv;
+  *(f32x4*)(op + 16) = a1 * inv;
+  if (q == 0 && half == 0 && g == 0 && p.lse)
+    p.lse[oh] = L > 0.f ? (M + __log2f(L)) * kLn2 : -__builtin_huge_valf();
 }
 
 hipError_t launch_attn_combine(const AttnPlan& p, hipStream_t s) {
