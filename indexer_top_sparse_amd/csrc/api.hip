@@ -47,8 +47,9 @@ struct IndexLayout {
   int rows = 0;        // B * R
   int n_units = 0;
   int n_chunks = 0;
-  size_t scores = 0, hist = 0, cand_key = 0, cand_idx = 0, chunk_cnt = 0,
-         depth = 0, plane_w = 0, score_c = 0, end = 0;
+  int hist_parts = 0;   // histogram parts per row the score kernel writes
+  size_t scores = 0, hist = 0, bstar = 0, cand_key = 0, cand_idx = 0, chunk_cnt = 0,
+         depth = 0, plist = 0, pwl = 0, npl = 0, score_c = 0, end = 0;
 };
 
 IndexLayout index_layout(const sparse_index_args& a, bool with_scores) {
@@ -62,14 +63,21 @@ IndexLayout index_layout(const sparse_index_args& a, bool with_scores) {
   auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
   const size_t cells = (size_t)L.rows * L.n_units;
   L.scores = with_scores ? take(cells * 4) : 0;
-  L.hist = take((size_t)L.rows * sd::kHistStride * 4);
+  // room for the score kernel's parts and for one part per chunk (the
+  // standalone top-k)
+  L.hist_parts = sd::score_hist_parts(a);
+  const int parts = std::max(L.hist_parts, std::max(L.n_chunks, 1));
+  L.hist = take((size_t)L.rows * parts * sd::kHistWords * 4);
+  L.bstar = take((size_t)L.rows * 2 * 4);
   L.cand_key = take(cells * 4);
   L.cand_idx = take(cells * 4);
   L.chunk_cnt = take((size_t)L.rows * std::max(L.n_chunks, 1) * 4);
   if (a.kind == SPARSE_SCORE_BITPLANE) {
     const size_t hd = (size_t)a.batch * a.n_kv_heads * a.head_dim;
     L.depth = take(hd);
-    L.plane_w = take(hd * 4 * 4);
+    L.plist = take(hd * 4 * 4);
+    L.pwl = take(hd * 4 * 4);
+    L.npl = take((size_t)a.batch * a.n_kv_heads * 4);
     L.score_c = take((size_t)a.batch * a.n_kv_heads * 4);
   }
   L.end = off;
@@ -222,7 +230,8 @@ int check_attn(const sparse_attn_args* a, int sel_heads, int k, int sel_unit) {
 
 sd::TopkPlan make_topk_plan(const IndexLayout& L, char* ws, const float* scores,
                             int64_t row_stride, const int32_t* valid, int rows_per_valid,
-                            int unit_div, int k, int32_t* idx_out, float* val_out) {
+                            int unit_div, int k, int32_t* idx_out, float* val_out,
+                            int hist_parts) {
   sd::TopkPlan p;
   p.rows = L.rows;
   p.n_units = L.n_units;
@@ -234,6 +243,8 @@ sd::TopkPlan make_topk_plan(const IndexLayout& L, char* ws, const float* scores,
   p.valid = valid;
   p.unit_div = unit_div;
   p.hist = (uint32_t*)(ws + L.hist);
+  p.parts = hist_parts;
+  p.bstar = (uint32_t*)(ws + L.bstar);
   p.cand_key = (uint32_t*)(ws + L.cand_key);
   p.cand_idx = (int32_t*)(ws + L.cand_idx);
   p.chunk_cnt = (uint32_t*)(ws + L.chunk_cnt);
@@ -249,10 +260,7 @@ int run_topk(const sd::TopkPlan& p, bool hist_ready, hipStream_t s) {
     HIPCHECK(sd::launch_topk_select(p, s));
     return SPARSE_OK;
   }
-  if (!hist_ready) {
-    HIPCHECK(sd::launch_zero_u32(p.hist, (int64_t)p.rows * sd::kHistStride, s));
-    HIPCHECK(sd::launch_topk_hist(p, s));
-  }
+  if (!hist_ready) HIPCHECK(sd::launch_topk_hist(p, s));
   HIPCHECK(sd::launch_topk_bin(p, s));
   HIPCHECK(sd::launch_topk_filter(p, s));
   HIPCHECK(sd::launch_topk_select(p, s));
@@ -267,7 +275,9 @@ int run_scores(const sparse_index_args& a, const IndexLayout& L, char* ws, float
   sp.hist = hist;
   sp.n_units = L.n_units;
   sp.depth = nullptr;
-  sp.plane_w = nullptr;
+  sp.plist = nullptr;
+  sp.pwl = nullptr;
+  sp.npl = nullptr;
   sp.score_c = nullptr;
   switch (a.kind) {
     case SPARSE_SCORE_DOT:
@@ -278,9 +288,11 @@ int run_scores(const sparse_index_args& a, const IndexLayout& L, char* ws, float
       break;
     case SPARSE_SCORE_BITPLANE:
       sp.depth = (int8_t*)(ws + L.depth);
-      sp.plane_w = (float*)(ws + L.plane_w);
+      sp.plist = (int32_t*)(ws + L.plist);
+      sp.pwl = (float*)(ws + L.pwl);
+      sp.npl = (int32_t*)(ws + L.npl);
       sp.score_c = (float*)(ws + L.score_c);
-      HIPCHECK(sd::launch_read_depth(&a, sp.depth, sp.plane_w, sp.score_c, s));
+      HIPCHECK(sd::launch_read_depth(&a, sp.depth, sp.plist, sp.pwl, sp.npl, sp.score_c, s));
       HIPCHECK(sd::launch_score_bitplane(sp, s));
       break;
   }
@@ -371,7 +383,7 @@ int sparse_read_depth(const sparse_index_args* ia, int8_t* depth_out, void* stre
   CHECK(ia->q, SPARSE_EINVAL, "q NULL");
   // the scan weights are a by-product the kernel skips when given NULL
   hipStream_t s = (hipStream_t)stream;
-  HIPCHECK(sd::launch_read_depth(ia, depth_out, nullptr, nullptr, s));
+  HIPCHECK(sd::launch_read_depth(ia, depth_out, nullptr, nullptr, nullptr, nullptr, s));
   return SPARSE_OK;
 }
 
@@ -410,7 +422,8 @@ int sparse_topk(const float* scores, int32_t rows, int32_t n_units, int64_t row_
   a.block_size = 1;
   IndexLayout L = index_layout(a, false);
   sd::TopkPlan p = make_topk_plan(L, (char*)ws, scores, row_stride, valid_units,
-                                  valid_units ? rows_per_valid : 1, 1, k, idx_out, val_out);
+                                  valid_units ? rows_per_valid : 1, 1, k, idx_out, val_out,
+                                  L.n_chunks);
   return run_topk(p, false, (hipStream_t)stream);
 }
 
@@ -454,9 +467,8 @@ int sparse_decode_step(const sparse_index_args* ia, const sparse_attn_args* aa, 
   IndexLayout L = index_layout(*ia, true);
   float* scores = (float*)(w + L.scores);
   sd::TopkPlan tp = make_topk_plan(L, w, scores, L.n_units, ia->seq_lens, L.rows_per_b,
-                                   unit, k, topk_out, nullptr);
+                                   unit, k, topk_out, nullptr, L.hist_parts);
   if (ia->n > 0) {
-    HIPCHECK(sd::launch_zero_u32(tp.hist, (int64_t)tp.rows * sd::kHistStride, s));
     rc = run_scores(*ia, L, w, scores, tp.hist, s);
     if (rc) return rc;
   }

@@ -806,33 +806,61 @@ hipError_t launch_attn_bf16(const AttnPlan& p, hipStream_t s) {
 // ================================================================ combine
 // Merge split partials of one (request, head): M = max m_s,
 // L = sum l_s exp(m_s - M), out = sum o_s exp(m_s - M) / L, lse = M + log L.
-// One workgroup per (request, head); each thread merges four columns.
-__global__ __launch_bounds__(128) void attn_combine_kernel(AttnPlan p) {
+constexpr int kCombThreads = 256;
+
+// One workgroup per (request, head); thread (q, sl) merges column quad q
+// (d_v / 4 quads, d_v <= 512) over splits sl, sl + SL, ... (SL = threads per
+// quad), and the SL partial results are summed through LDS.
+__global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(AttnPlan p) {
+  __shared__ float m_s[kCombThreads];
+  __shared__ f32x4 acc_s[kCombThreads];
+  __shared__ float l_s[kCombThreads];
   const sparse_attn_args& A = p.a;
   const int dv = A.d_v;
   const int S = p.splits;
   const int64_t oh = blockIdx.x;
   const float* pp = p.part + oh * S * (dv + 4);
-  float M = -__builtin_huge_valf();
-  for (int s = 0; s < S; ++s) M = fmaxf(M, pp[s * (dv + 4) + dv]);
-  float L = 0.f;
+  const int tid = threadIdx.x;
+  const int Q = dv / 4;
+  const int SL = kCombThreads / Q;
+  const int q = tid % Q, sl = tid / Q;
+  // M = max over splits of the split maxima
+  float mloc = -__builtin_huge_valf();
+  for (int sp = tid; sp < S; sp += kCombThreads) mloc = fmaxf(mloc, pp[(int64_t)sp * (dv + 4) + dv]);
+  m_s[tid] = mloc;
+  __syncthreads();
+  for (int off = kCombThreads / 2; off >= 1; off >>= 1) {
+    if (tid < off) m_s[tid] = fmaxf(m_s[tid], m_s[tid + off]);
+    __syncthreads();
+  }
+  const float M = m_s[0];
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  const int c = 4 * threadIdx.x;
-  for (int s = 0; s < S; ++s) {
-    const float* ps = pp + s * (dv + 4);
-    const float l = ps[dv + 1];
-    if (l > 0.f) {
-      const float f = __expf(ps[dv] - M);
+  float L = 0.f;
+  if (sl < SL) {
+#pragma unroll 4
+    for (int sp = sl; sp < S; sp += SL) {
+      const float* ps = pp + (int64_t)sp * (dv + 4);
+      const float l = ps[dv + 1];
+      const float f = l > 0.f ? __expf(ps[dv] - M) : 0.f;
+      const f32x4 v = *(const f32x4*)(ps + 4 * q);
+      acc += v * f;
       L += l * f;
-      if (c < dv) {
-        const f32x4 v = *(const f32x4*)(ps + c);
-        acc += v * f;
-      }
     }
   }
-  const float inv = L > 0.f ? 1.f / L : 0.f;
-  if (c < dv) *(f32x4*)(p.out + oh * dv + c) = acc * inv;
-  if (threadIdx.x == 0 && p.lse) p.lse[oh] = L > 0.f ? M + __logf(L) : -__builtin_huge_valf();
+  acc_s[tid] = acc;
+  l_s[tid] = L;
+  __syncthreads();
+  if (tid < Q) {
+    f32x4 a = acc_s[tid];
+    float Lt = l_s[tid];
+    for (int k = 1; k < SL; ++k) {
+      a += acc_s[tid + k * Q];
+      Lt += l_s[tid + k * Q];
+    }
+    const float inv = Lt > 0.f ? 1.f / Lt : 0.f;
+    *(f32x4*)(p.out + oh * dv + 4 * tid) = a * inv;
+    if (tid == 0 && p.lse) p.lse[oh] = Lt > 0.f ? M + __logf(Lt) : -__builtin_huge_valf();
+  }
 }
 
 // Latent records (register order of the attention kernel, base-2 m): one
@@ -880,7 +908,7 @@ hipError_t launch_attn_combine(const AttnPlan& p, hipStream_t s) {
     const int64_t wgs = (int64_t)a.batch * (a.n_q_heads / kMlaHeadsWG) * kMlaWaves;
     attn_combine_mla_kernel<<<(unsigned)wgs, 512, 0, s>>>(p);
   } else {
-    attn_combine_kernel<<<(unsigned)((int64_t)a.batch * a.n_q_heads), 128, 0, s>>>(p);
+    attn_combine_kernel<<<(unsigned)((int64_t)a.batch * a.n_q_heads), kCombThreads, 0, s>>>(p);
   }
   return hipGetLastError();
 }

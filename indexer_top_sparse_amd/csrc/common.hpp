@@ -20,11 +20,13 @@ constexpr int kWave = 64;
 
 constexpr int kTopkChunk = 4096;
 constexpr int kHistBins = 4096;
-// A histogram row: 4096 bins, then the boundary bin b* that holds the
-// k-th largest key and the count of units in higher bins.
-constexpr int kHistStride = kHistBins + 4;
-constexpr int kHistBstar = kHistBins;
-constexpr int kHistAbove = kHistBins + 1;
+// Histograms of the first radix digit (the top 12 key bits) are written in
+// parts: every producing workgroup stores its own 4096 16-bit counts (two
+// per 32-bit word), so no global atomics and no clearing are needed, and
+// the bin kernel sums the parts of a row.  A part never counts more than
+// kHistPartMax units.
+constexpr int kHistWords = kHistBins / 2;
+constexpr int kHistPartMax = 65535;
 
 // Pointer into the global address space: loads through it compile to
 // global_load (vector memory counter only) rather than flat_load.
@@ -124,7 +126,9 @@ struct TopkPlan {
   const float* scores;
   const int32_t* valid;
   int32_t unit_div;  // valid units = ceil(valid / unit_div)
-  uint32_t* hist;    // [rows][kHistStride]
+  uint32_t* hist;    // [rows][parts][kHistWords] 16-bit counts in pairs
+  int parts;         // histogram parts per row
+  uint32_t* bstar;   // [rows][2]: boundary bin b*, units in higher bins
   uint32_t* cand_key;  // [rows][n_units]
   int32_t* cand_idx;   // [rows][n_units]
   uint32_t* chunk_cnt; // [rows][n_chunks]
@@ -133,7 +137,6 @@ struct TopkPlan {
 };
 
 
-hipError_t launch_zero_u32(uint32_t* p, int64_t count, hipStream_t s);
 hipError_t launch_topk_hist(const TopkPlan& p, hipStream_t s);
 hipError_t launch_topk_bin(const TopkPlan& p, hipStream_t s);
 hipError_t launch_topk_filter(const TopkPlan& p, hipStream_t s);
@@ -142,16 +145,20 @@ hipError_t launch_topk_select(const TopkPlan& p, hipStream_t s);
 struct ScorePlan {
   const sparse_index_args* a;
   float* scores;     // [B][R][n_units]
-  uint32_t* hist;    // [B*R][kHistStride] (nullable: no fused histogram)
+  uint32_t* hist;    // [B*R][score_hist_parts][kHistWords] (nullable)
   int n_units;
   int8_t* depth;     // BITPLANE: [B][Hkv][D]
-  float* plane_w;    // BITPLANE: [B][Hkv][D][4] weight of each plane bit
+  int32_t* plist;    // BITPLANE: [B][Hkv][4D] read planes (index 4c + j), then
+  float* pwl;        //   their weights q_bar_c * cell_c * 2^(3-j)
+  int32_t* npl;      //   [B][Hkv] number of read planes
   float* score_c;    // BITPLANE: [B][Hkv] constant term
 };
+// Histogram parts per row that the score kernel of `a` writes.
+int score_hist_parts(const sparse_index_args& a);
 hipError_t launch_score_dot(const ScorePlan& p, hipStream_t s);
 hipError_t launch_score_lightning(const ScorePlan& p, hipStream_t s);
-hipError_t launch_read_depth(const sparse_index_args* a, int8_t* depth,
-                             float* plane_w, float* score_c, hipStream_t s);
+hipError_t launch_read_depth(const sparse_index_args* a, int8_t* depth, int32_t* plist,
+                             float* pwl, int32_t* npl, float* score_c, hipStream_t s);
 hipError_t launch_score_bitplane(const ScorePlan& p, hipStream_t s);
 
 struct AttnPlan {

@@ -1,23 +1,36 @@
 // Index scores (step a2) and Fathom read depth (step a1).
 //
 // Every kernel here streams the HBM-resident index once, keeps the query in
-// registers, writes fp32 unit scores and, when asked, adds each valid unit's
-// top-12-bit key to a per-row 4096-bin histogram (the first radix digit of
-// the top-k select) so the select never re-reads the scores for it.
+// registers, writes fp32 unit scores and, when asked, counts each valid
+// unit's top-12-bit key in a 4096-bin LDS histogram (the first radix digit
+// of the top-k select) that the workgroup stores as its own part of the
+// row's histogram, so the select never re-reads the scores for it.
+#include <algorithm>
+
 #include "common.hpp"
 
 namespace sd {
 
-// Per-workgroup histogram in LDS, flushed to the row's global histogram.
+// max(0, x) as one integer max on the bit pattern: non-negative floats are
+// non-negative integers, negative floats (and -0) are negative integers.
+// Unlike fmaxf it needs no NaN canonicalisation of MFMA results.
+__device__ __forceinline__ float relu_bits(float x) {
+  return __int_as_float(max(__float_as_int(x), 0));
+}
+
+// Per-workgroup histogram in LDS, stored as one part of its row's
+// histogram: 16-bit counts, two per word (a workgroup counts at most
+// kHistPartMax units).  clear() ends with a barrier.
 struct LdsHist {
   uint32_t* h;
   __device__ void clear(int nt) {
     for (int i = threadIdx.x; i < kHistBins; i += nt) h[i] = 0u;
+    __syncthreads();
   }
   __device__ void add(float s) { atomicAdd(&h[score_key(s) >> 20], 1u); }
-  __device__ void flush(uint32_t* g, int nt) {
-    for (int i = threadIdx.x; i < kHistBins; i += nt)
-      if (h[i]) atomicAdd(&g[i], h[i]);
+  __device__ void store(uint32_t* part, int nt) {
+    for (int i = threadIdx.x; i < kHistWords; i += nt)
+      part[i] = h[2 * i] | (h[2 * i + 1] << 16);
   }
 };
 
@@ -66,6 +79,7 @@ __device__ __forceinline__ void load_elems(const uint16_t* p, float* x) {
 
 constexpr int kDotThreads = 256;
 constexpr int kDotTokensPerWG = 2048;
+static_assert(kDotTokensPerWG <= kHistPartMax, "histogram part overflow");
 
 template <typename T, int BLOCK>
 __global__ __launch_bounds__(kDotThreads) void score_dot_kernel(
@@ -160,8 +174,7 @@ __global__ __launch_bounds__(kDotThreads) void score_dot_kernel(
   }
   if (hist) {
     __syncthreads();
-    uint32_t* g = hist + (int64_t)b * kHistStride;
-    lh.flush(g, kDotThreads);
+    lh.store(hist + ((int64_t)b * gridDim.x + blockIdx.x) * kHistWords, kDotThreads);
   }
 }
 
@@ -317,7 +330,7 @@ __global__ __launch_bounds__(kLtThreads) void score_lightning_kernel(
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) sum = fmaf(wv[mt][e], fmaxf(acc[mt][e], 0.f), sum);
+      for (int e = 0; e < 16; ++e) sum = fmaf(wv[mt][e], relu_bits(acc[mt][e]), sum);
     // lanes l and l^32 hold the two halves of the heads of the same token
     float other = swap_halves(sum);
     float total = half ? other + sum : sum + other;
@@ -358,20 +371,29 @@ __global__ __launch_bounds__(kLtThreads) void score_lightning_kernel(
   }
   if (hist) {
     __syncthreads();
-    uint32_t* g = hist + (int64_t)b * kHistStride;
-    lh.flush(g, kLtThreads);
+    lh.store(hist + ((int64_t)b * gridDim.x + blockIdx.x) * kHistWords, kLtThreads);
   }
+}
+
+// long spans per workgroup (fewer histogram clears and stores) when the
+// batch still gives at least two workgroups per compute unit
+constexpr int kLtLong = 64, kLtShort = 16;
+static_assert(kLtLong * kLtStride <= kHistPartMax, "histogram part overflow");
+bool lightning_long(const sparse_index_args& a) {
+  const int64_t long_wgs =
+      (int64_t)a.batch * ((a.n + kLtLong * kLtStride - 1) / (kLtLong * kLtStride));
+  return long_wgs >= 512;
+}
+int lightning_parts(const sparse_index_args& a) {
+  const int span = (lightning_long(a) ? kLtLong : kLtShort) * kLtStride;
+  return (a.n + span - 1) / span;
 }
 
 hipError_t launch_score_lightning(const ScorePlan& p, hipStream_t s) {
   const sparse_index_args& a = *p.a;
-  // long spans per workgroup (fewer histogram clears and flushes) when the
-  // batch still gives at least two workgroups per compute unit
-  constexpr int kLong = 64, kShort = 16;
-  const int64_t long_wgs = (int64_t)a.batch * ((a.n + kLong * kLtStride - 1) / (kLong * kLtStride));
-  const bool use_long = long_wgs >= 512;
-  const int span = (use_long ? kLong : kShort) * kLtStride;
-  dim3 grid((a.n + span - 1) / span, a.batch);
+  constexpr int kLong = kLtLong, kShort = kLtShort;
+  const bool use_long = lightning_long(a);
+  dim3 grid(lightning_parts(a), a.batch);
   if (a.n_heads == 64) {
     if (use_long) score_lightning_kernel<64, kLong><<<grid, kLtThreads, 0, s>>>(a, p.scores, p.hist, p.n_units);
     else score_lightning_kernel<64, kShort><<<grid, kLtThreads, 0, s>>>(a, p.scores, p.hist, p.n_units);
@@ -394,14 +416,16 @@ hipError_t launch_score_lightning(const ScorePlan& p, hipStream_t s) {
 // sum_c q_bar_c * (zero_c + cell_c * 2^(3 - t_c)).
 // ========================================================================
 constexpr int kDepthThreads = 512;  // D = 128 channels x 4 planes
+constexpr int kPlaneBatch = 8;      // plane-list entries the scan fetches at once
 
 __global__ __launch_bounds__(kDepthThreads) void read_depth_kernel(
-    sparse_index_args a, int8_t* __restrict__ depth, float* __restrict__ plane_w,
-    float* __restrict__ score_c) {
+    sparse_index_args a, int8_t* __restrict__ depth, int32_t* __restrict__ plist,
+    float* __restrict__ pwl, int32_t* __restrict__ npl, float* __restrict__ score_c) {
   __shared__ double gain_s[kDepthThreads];
   __shared__ double qbar_s[128];
   __shared__ int taken_s[kDepthThreads];
   __shared__ double cterm_s[128];
+  __shared__ int scan_s[kDepthThreads / 64 + 1];
   const int h = blockIdx.x;
   const int b = blockIdx.y;
   const int D = a.head_dim;
@@ -426,21 +450,33 @@ __global__ __launch_bounds__(kDepthThreads) void read_depth_kernel(
     gain_s[tid] = ldexp(imp, -2 * j);
   }
   __syncthreads();
-  int taken = 0;
-  if (c < D) {
-    const double g = gain_s[tid];
-    int rank = 0;
-    const int tot = 4 * D;
-    for (int o = 0; o < tot; ++o) {
-      double go = gain_s[o];
-      // o precedes tid in (gain desc, channel asc, plane asc); index order
-      // o < tid is exactly (channel, plane) ascending
-      rank += (go > g) || (go == g && o < tid);
+  // Rank every gain in the total order (gain desc, channel asc, plane asc)
+  // -- index order tid = 4c + j is (channel, plane) ascending -- with a
+  // bitonic sort of (gain, index) pairs: position r of the sorted list holds
+  // the gain of rank r.  Slots past 4D hold -1 (below every gain).
+  {
+    double key = c < D ? gain_s[tid] : -1.0;
+    int id = tid;
+    for (int k = 2; k <= kDepthThreads; k <<= 1) {
+      for (int jj = k >> 1; jj > 0; jj >>= 1) {
+        __syncthreads();
+        gain_s[tid] = key;
+        taken_s[tid] = id;
+        __syncthreads();
+        const int o = tid ^ jj;
+        const double ko = gain_s[o];
+        const int io = taken_s[o];
+        const bool mine_first = (key > ko) || (key == ko && id < io);
+        // the lower slot of an ascending block keeps the earlier element
+        const bool keep_first = ((tid & k) == 0) == (tid < o);
+        if (mine_first != keep_first) { key = ko; id = io; }
+      }
     }
-    taken = rank < a.bit_budget;
+    __syncthreads();
+    taken_s[id] = tid < a.bit_budget;  // element id has rank tid
+    __syncthreads();
   }
-  taken_s[tid] = taken;
-  __syncthreads();
+  const int taken = c < D ? taken_s[tid] : 0;
   if (tid < D) {
     int t = taken_s[4 * tid] + taken_s[4 * tid + 1] + taken_s[4 * tid + 2] +
             taken_s[4 * tid + 3];
@@ -450,11 +486,23 @@ __global__ __launch_bounds__(kDepthThreads) void read_depth_kernel(
     double zero = (double)a.chan_zero[hd + tid];
     cterm_s[tid] = qb * (zero + cell * ldexp(1.0, 3 - t));
   }
-  if (plane_w && c < D) {
-    double qb = qbar_s[c];
-    double cell = (double)a.chan_scale[hd + c];
-    // weight of plane j of channel c when it is read (0 otherwise)
-    plane_w[hd * 4 + tid] = taken ? (float)(qb * cell * ldexp(1.0, 3 - j)) : 0.f;
+  if (plist) {
+    // read planes in (channel, plane) order with the weight of their bit
+    int total;
+    const int incl = block_inclusive_scan<kDepthThreads>(taken, scan_s, &total);
+    if (taken) {
+      const double qb = qbar_s[c];
+      const double cell = (double)a.chan_scale[hd + c];
+      plist[hd * 4 + incl - 1] = tid;
+      pwl[hd * 4 + incl - 1] = (float)(qb * cell * ldexp(1.0, 3 - j));
+    }
+    if (tid == 0) npl[(int64_t)b * Hkv + h] = total;
+    // pad the list to a multiple of kPlaneBatch with weightless plane 0
+    const int padded = (total + kPlaneBatch - 1) / kPlaneBatch * kPlaneBatch;
+    if (tid >= total && tid < padded) {
+      plist[hd * 4 + tid] = 0;
+      pwl[hd * 4 + tid] = 0.f;
+    }
   }
   __syncthreads();
   if (score_c && tid == 0) {
@@ -464,29 +512,46 @@ __global__ __launch_bounds__(kDepthThreads) void read_depth_kernel(
   }
 }
 
-hipError_t launch_read_depth(const sparse_index_args* a, int8_t* depth,
-                             float* plane_w, float* score_c, hipStream_t s) {
+hipError_t launch_read_depth(const sparse_index_args* a, int8_t* depth, int32_t* plist,
+                             float* pwl, int32_t* npl, float* score_c, hipStream_t s) {
   dim3 grid(a->n_kv_heads, a->batch);
-  read_depth_kernel<<<grid, kDepthThreads, 0, s>>>(*a, depth, plane_w, score_c);
+  read_depth_kernel<<<grid, kDepthThreads, 0, s>>>(*a, depth, plist, pwl, npl, score_c);
   return hipGetLastError();
 }
 
 // ========================================================================
-// Fathom plane-prefix scan.  Thread = one 32-token word column of a
-// (request, KV head); for each read plane (c, j) it loads that plane's word
-// (coalesced across threads) and adds W_{c,j} to the tokens whose bit is
-// set.  The list of read planes is compacted once per workgroup in LDS.
+// Fathom plane-prefix scan.  A thread owns one 32-bit word column of a
+// (request, KV head): 32 consecutive tokens.  For each read plane (c, j)
+// from the list read_depth_kernel wrote it loads that plane's word
+// (coalesced across the workgroup) and adds the plane weight W_{c,j} to the
+// tokens whose bit is set; the bit becomes an all-ones or all-zero mask of
+// the weight's bits (sign-extending bit field), so a token costs one
+// extract, one AND and one add per plane.  Loads run kBpUnroll planes
+// ahead of their use.
 // ========================================================================
-constexpr int kBpThreads = 256;
+constexpr int kBpThreads = 1024;
+constexpr int kBpPassTok = kBpThreads * 32;             // 32768 tokens per workgroup pass
+constexpr int kBpMaxPasses = kHistPartMax / kBpPassTok;  // per workgroup (histogram part)
+constexpr int kBpUnroll = 4;
+static_assert(kPlaneBatch % kBpUnroll == 0, "padded plane list");
+
+int bitplane_parts(const sparse_index_args& a) {
+  const int passes = (a.n + kBpPassTok - 1) / kBpPassTok;
+  const int rows = a.batch * a.n_kv_heads;
+  // about 256 workgroups (one per compute unit) in all, each within one
+  // histogram part's capacity
+  int parts = (int)std::max<int64_t>(1, (256 + rows - 1) / std::max(rows, 1));
+  parts = std::min(parts, passes);
+  parts = std::max(parts, (passes + kBpMaxPasses - 1) / kBpMaxPasses);
+  return std::max(parts, 1);
+}
 
 __global__ __launch_bounds__(kBpThreads) void score_bitplane_kernel(
-    sparse_index_args a, const float* __restrict__ plane_w,
-    const float* __restrict__ score_c, float* __restrict__ scores,
-    uint32_t* hist, int n_units) {
+    sparse_index_args a, const int32_t* plist, const float* pwl, const int32_t* npl,
+    const float* score_c, float* __restrict__ scores, uint32_t* hist, int n_units) {
   __shared__ uint32_t hist_s[kHistBins];
-  __shared__ int plist_s[512];
+  __shared__ int32_t pl_s[512];
   __shared__ float pw_s[512];
-  __shared__ int np_s;
   LdsHist lh{hist_s};
   const int h = blockIdx.y;
   const int b = blockIdx.z;
@@ -495,58 +560,74 @@ __global__ __launch_bounds__(kBpThreads) void score_bitplane_kernel(
   const int n = a.n;
   const int nw = (n + 31) / 32;
   const int valid = valid_len(a.seq_lens, b, n);
-  const int64_t hd = ((int64_t)b * Hkv + h) * D;
-  if (hist) lh.clear(kBpThreads);
-  if (threadIdx.x == 0) {
-    int cnt = 0;
-    for (int i = 0; i < 4 * D; ++i) {
-      float wgt = plane_w[hd * 4 + i];
-      // read planes are exactly those with a recorded weight slot; a zero
-      // weight adds nothing, so skipping it leaves the score unchanged
-      if (wgt != 0.f) { plist_s[cnt] = i; pw_s[cnt] = wgt; ++cnt; }
-    }
-    np_s = cnt;
+  const int64_t bh = (int64_t)b * Hkv + h;
+  const int np = npl[bh];
+  // the padded list (weightless entries up to a multiple of kPlaneBatch)
+  const int npad = (np + kPlaneBatch - 1) / kPlaneBatch * kPlaneBatch;
+  for (int i = threadIdx.x; i < npad; i += kBpThreads) {
+    pl_s[i] = plist[bh * 4 * D + i];
+    pw_s[i] = pwl[bh * 4 * D + i];
   }
-  __syncthreads();
-  const int np = np_s;
-  const float c0 = score_c[(int64_t)b * Hkv + h];
-  const uint32_t* pl = a.planes + hd * 4 * (int64_t)nw;
-  const int w = blockIdx.x * kBpThreads + threadIdx.x;
-  float* srow = scores + ((int64_t)b * Hkv + h) * n_units;
-  if (w < nw) {
+  if (hist) lh.clear(kBpThreads);  // (ends with a barrier)
+  else __syncthreads();
+  const float c0 = score_c[bh];
+  const uint32_t* planes = a.planes + bh * 4 * D * (int64_t)nw;
+  float* srow = scores + bh * n_units;
+  const int passes = (n + kBpPassTok - 1) / kBpPassTok;
+  for (int ps = blockIdx.x; ps < passes; ps += gridDim.x) {
+    const int w = ps * kBpThreads + threadIdx.x;
+    const int wc = w < nw ? w : nw - 1;  // ragged end: a valid word, result unused
     float acc[32];
 #pragma unroll
     for (int i = 0; i < 32; ++i) acc[i] = c0;
-    for (int p = 0; p < np; ++p) {
-      uint32_t word = pl[(int64_t)plist_s[p] * nw + w];
-      float wgt = pw_s[p];
+    for (int p0 = 0; p0 < npad; p0 += kBpUnroll) {
+      uint32_t wd[kBpUnroll];
 #pragma unroll
-      for (int i = 0; i < 32; ++i) acc[i] += ((word >> i) & 1u) ? wgt : 0.f;
+      for (int k = 0; k < kBpUnroll; ++k)
+        wd[k] = __builtin_nontemporal_load(planes + (int64_t)pl_s[p0 + k] * nw + wc);
+#pragma unroll
+      for (int k = 0; k < kBpUnroll; ++k) {
+        const uint32_t wb = __float_as_uint(pw_s[p0 + k]);
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+          // bit i of the word, sign-extended: all ones or zero
+          const uint32_t m = (uint32_t)__builtin_amdgcn_sbfe((int)wd[k], i, 1);
+          acc[i] += __uint_as_float(wb & m);
+        }
+      }
     }
+    if (w < nw) {
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      int t = 32 * w + i;
-      float s = t < valid ? acc[i] : -__builtin_huge_valf();
-      if (t < n) {
-        srow[t] = s;
-        if (hist && t < valid) lh.add(s);
+      for (int i = 0; i < 32; ++i) {
+        const int t = 32 * w + i;
+        const float sc = t < valid ? acc[i] : -__builtin_huge_valf();
+        if (t < n) {
+          srow[t] = sc;
+          if (hist && t < valid) lh.add(sc);
+        }
       }
     }
   }
   if (hist) {
     __syncthreads();
-    uint32_t* g = hist + ((int64_t)b * Hkv + h) * kHistStride;
-    lh.flush(g, kBpThreads);
+    lh.store(hist + (bh * gridDim.x + blockIdx.x) * kHistWords, kBpThreads);
   }
 }
 
 hipError_t launch_score_bitplane(const ScorePlan& p, hipStream_t s) {
   const sparse_index_args& a = *p.a;
-  const int nw = (a.n + 31) / 32;
-  dim3 grid((nw + kBpThreads - 1) / kBpThreads, a.n_kv_heads, a.batch);
-  score_bitplane_kernel<<<grid, kBpThreads, 0, s>>>(a, p.plane_w, p.score_c,
+  dim3 grid(bitplane_parts(a), a.n_kv_heads, a.batch);
+  score_bitplane_kernel<<<grid, kBpThreads, 0, s>>>(a, p.plist, p.pwl, p.npl, p.score_c,
                                                    p.scores, p.hist, p.n_units);
   return hipGetLastError();
+}
+
+int score_hist_parts(const sparse_index_args& a) {
+  switch (a.kind) {
+    case SPARSE_SCORE_DOT: return (a.n + kDotTokensPerWG - 1) / kDotTokensPerWG;
+    case SPARSE_SCORE_LIGHTNING: return lightning_parts(a);
+    default: return bitplane_parts(a);
+  }
 }
 
 }  // namespace sd

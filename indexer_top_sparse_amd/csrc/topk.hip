@@ -6,37 +6,24 @@
 // the k indices come out ascending.
 //
 // Design (radix select on order-preserving 32-bit keys, few long rows):
-//   hist    rows x chunks workgroups: a 4096-bin histogram of the top 12 key
-//           bits of every valid unit (LDS, then global atomics).  The fused
-//           score kernels build the same histogram while they write scores.
-//   bin     one workgroup per row: the bin b* holding the k-th largest key,
-//           and the count of units above it.
+//   hist    rows x chunks workgroups: each counts the top 12 key bits of
+//           its chunk's valid units in a 4096-bin LDS histogram and stores it
+//           as one 16-bit part of the row's histogram.  The fused score
+//           kernels store the same parts while they write scores.
+//   bin     one workgroup per row: sums the row's parts, finds the bin b*
+//           holding the k-th largest key and the count of units above it.
 //   filter  rows x chunks workgroups: compacts, in index order, every unit
 //           whose bin is >= b* into its chunk's slice of a candidate buffer
-//           (keys and indices) and stores the chunk count.
-//   select  one workgroup per row: stages the candidates in LDS and resolves
-//           the remaining 20 key bits over those of bin b* (two histogram
-//           passes), which
-//           gives the exact k-th key T and how many units equal to T are
-//           needed, then writes the selection in index order with block
-//           prefix sums (ties to the lowest indices).
+//           (keys and indices) and stores the chunk count (one block scan).
+//   select  one workgroup per row: stages the candidates in LDS chunk by
+//           chunk while counting bits [19:8] of those in bin b*, resolves
+//           the last 8 bits in a second LDS histogram, which gives the exact
+//           k-th key T and how many units equal to T are needed, then
+//           writes the selection in index order with block prefix sums
+//           (ties to the lowest indices).
 #include "common.hpp"
 
 namespace sd {
-
-__global__ void zero_u32_kernel(uint32_t* __restrict__ p, int64_t count) {
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (; i < count; i += stride) p[i] = 0u;
-}
-
-hipError_t launch_zero_u32(uint32_t* p, int64_t count, hipStream_t s) {
-  if (count <= 0) return hipSuccess;
-  int64_t blocks = (count + 255) / 256;
-  if (blocks > 4096) blocks = 4096;
-  zero_u32_kernel<<<(unsigned)blocks, 256, 0, s>>>(p, count);
-  return hipGetLastError();
-}
 
 __device__ __forceinline__ int row_valid_units(const TopkPlan& p, int r) {
   int v = p.n_units;
@@ -49,6 +36,8 @@ __device__ __forceinline__ int row_valid_units(const TopkPlan& p, int r) {
 }
 
 // --------------------------------------------------------------------- hist
+// Part c of row r's histogram: the valid units of chunk c (p.parts must be
+// p.n_chunks).
 __global__ __launch_bounds__(256) void topk_hist_kernel(TopkPlan p) {
   __shared__ uint32_t h[kHistBins];
   const int r = blockIdx.y;
@@ -62,9 +51,9 @@ __global__ __launch_bounds__(256) void topk_hist_kernel(TopkPlan p) {
   for (int u = lo + threadIdx.x; u < hi; u += 256)
     atomicAdd(&h[score_key(row[u]) >> 20], 1u);
   __syncthreads();
-  uint32_t* g = p.hist + (int64_t)r * kHistStride;
-  for (int i = threadIdx.x; i < kHistBins; i += 256)
-    if (h[i]) atomicAdd(&g[i], h[i]);
+  uint32_t* part = p.hist + ((int64_t)r * p.parts + c) * kHistWords;
+  for (int i = threadIdx.x; i < kHistWords; i += 256)
+    part[i] = h[2 * i] | (h[2 * i + 1] << 16);
 }
 
 hipError_t launch_topk_hist(const TopkPlan& p, hipStream_t s) {
@@ -105,25 +94,55 @@ __device__ void find_bin_from_top(const uint32_t* hist, int nbins, int need,
 }
 
 // --------------------------------------------------------------------- bin
-// One workgroup per row: the bin b* holding the k_eff-th largest key of the
-// complete histogram, and the number of units in higher bins, stored in the
-// row's tail for the filter and select kernels.
-constexpr int kBinThreads = 512;
+// One workgroup per row: sums the row's histogram parts, then the bin b*
+// holding the k_eff-th largest key and the number of units in higher bins.
+constexpr int kBinThreads = 1024;
+constexpr int kBinGroups = kBinThreads / (kHistWords / 4);  // 2 part groups
+constexpr int kBinUnroll = 8;
 
 __global__ __launch_bounds__(kBinThreads) void topk_bin_kernel(TopkPlan p) {
-  __shared__ uint32_t hs[kHistBins];
+  __shared__ uint32_t hs[kBinGroups][kHistBins];
   __shared__ int scan_lds[kBinThreads / 64 + 1];
   __shared__ int res[2];
   const int r = blockIdx.x;
+  const int t = threadIdx.x;
   const int k_eff = min(p.k, row_valid_units(p, r));
-  uint32_t* g = p.hist + (int64_t)r * kHistStride;
-  for (int i = threadIdx.x; i < kHistBins; i += kBinThreads) hs[i] = g[i];
-  if (threadIdx.x == 0) { res[0] = 0; res[1] = 0; }
+  // thread t: words 4 (t % 512) .. +3 (bins 8 (t % 512) .. +7) of parts
+  // t / 512, t / 512 + 2, ...; kBinUnroll loads in flight
+  const int grp = t / (kHistWords / 4);
+  const int wq = t % (kHistWords / 4);
+  const uint32_t* base = p.hist + (int64_t)r * p.parts * kHistWords + 4 * wq;
+  uint32_t cnt[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int q0 = grp; q0 < p.parts; q0 += kBinGroups * kBinUnroll) {
+    u32x4 w[kBinUnroll];
+#pragma unroll
+    for (int u = 0; u < kBinUnroll; ++u) {
+      const int q = q0 + u * kBinGroups;
+      w[u] = q < p.parts ? *(const u32x4*)(base + (int64_t)q * kHistWords) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < kBinUnroll; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        cnt[2 * e] += w[u][e] & 0xFFFFu;
+        cnt[2 * e + 1] += w[u][e] >> 16;
+      }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) hs[grp][8 * wq + e] = cnt[e];
+  if (t == 0) { res[0] = 0; res[1] = 0; }
   __syncthreads();
-  if (k_eff > 0) find_bin_from_top<kBinThreads>(hs, kHistBins, k_eff, scan_lds, res);
-  if (threadIdx.x == 0) {
-    g[kHistBstar] = (uint32_t)res[0];
-    g[kHistAbove] = (uint32_t)res[1];
+  for (int i = t; i < kHistBins; i += kBinThreads) {
+    uint32_t x = hs[0][i];
+#pragma unroll
+    for (int gq = 1; gq < kBinGroups; ++gq) x += hs[gq][i];
+    hs[0][i] = x;
+  }
+  __syncthreads();
+  if (k_eff > 0) find_bin_from_top<kBinThreads>(hs[0], kHistBins, k_eff, scan_lds, res);
+  if (t == 0) {
+    p.bstar[2 * r] = (uint32_t)res[0];
+    p.bstar[2 * r + 1] = (uint32_t)res[1];
   }
 }
 
@@ -133,8 +152,14 @@ hipError_t launch_topk_bin(const TopkPlan& p, hipStream_t s) {
 }
 
 // ------------------------------------------------------------------- filter
-__global__ __launch_bounds__(256) void topk_filter_kernel(TopkPlan p) {
-  __shared__ int scan_lds[8];
+// One workgroup per (chunk, row); thread t owns the 16 consecutive units
+// lo + 16t .. lo + 16t + 15 of the chunk, so one block scan orders them all.
+constexpr int kFiltThreads = 256;
+constexpr int kFiltPer = kTopkChunk / kFiltThreads;  // 16
+static_assert(kFiltPer == 16, "four float4 loads per thread");
+
+__global__ __launch_bounds__(kFiltThreads) void topk_filter_kernel(TopkPlan p) {
+  __shared__ int scan_lds[kFiltThreads / 64 + 1];
   const int r = blockIdx.y;
   const int c = blockIdx.x;
   const int v = row_valid_units(p, r);
@@ -144,45 +169,53 @@ __global__ __launch_bounds__(256) void topk_filter_kernel(TopkPlan p) {
     if (threadIdx.x == 0) *cnt = 0u;
     return;
   }
-  const uint32_t bstar = p.hist[(int64_t)r * kHistStride + kHistBstar];
+  const uint32_t bstar = p.bstar[2 * r];
   const float* row = p.scores + (int64_t)r * p.row_stride;
   uint32_t* ck = p.cand_key + (int64_t)r * p.n_units + (int64_t)c * kTopkChunk;
   int32_t* ci = p.cand_idx + (int64_t)r * p.n_units + (int64_t)c * kTopkChunk;
   const int lo = c * kTopkChunk;
   const int hi = min(lo + kTopkChunk, v);
-  int base = 0;
-  for (int it = lo; it < hi; it += 256 * 4) {
-    const int u0 = it + threadIdx.x * 4;
-    uint32_t keys[4];
-    int flags = 0, cnt_t = 0;
+  const int u0 = lo + kFiltPer * threadIdx.x;
+  uint32_t keys[kFiltPer];
+  uint32_t flags = 0;
+  int n_t = 0;
+  if (u0 + kFiltPer <= hi && ((uintptr_t)(row + u0) & 15u) == 0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int u = u0 + i;
+    for (int i = 0; i < kFiltPer; i += 4) {
+      const f32x4 x = *(const f32x4*)(row + u0 + i);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) keys[i + e] = score_key(x[e]);
+    }
+#pragma unroll
+    for (int i = 0; i < kFiltPer; ++i)
+      if ((keys[i] >> 20) >= bstar) { flags |= 1u << i; ++n_t; }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kFiltPer; ++i) {
       keys[i] = 0u;
-      if (u < hi) {
-        keys[i] = score_key(row[u]);
-        if ((keys[i] >> 20) >= bstar) { flags |= 1 << i; ++cnt_t; }
+      if (u0 + i < hi) {
+        keys[i] = score_key(row[u0 + i]);
+        if ((keys[i] >> 20) >= bstar) { flags |= 1u << i; ++n_t; }
       }
     }
-    int total;
-    int incl = block_inclusive_scan<256>(cnt_t, scan_lds, &total);
-    int pos = base + incl - cnt_t;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (flags & (1 << i)) {
-        ck[pos] = keys[i];
-        ci[pos] = u0 + i;
-        ++pos;
-      }
-    }
-    base += total;
   }
-  if (threadIdx.x == 0) *cnt = (uint32_t)base;
+  int total;
+  const int incl = block_inclusive_scan<kFiltThreads>(n_t, scan_lds, &total);
+  int pos = incl - n_t;
+#pragma unroll
+  for (int i = 0; i < kFiltPer; ++i) {
+    if (flags & (1u << i)) {
+      ck[pos] = keys[i];
+      ci[pos] = u0 + i;
+      ++pos;
+    }
+  }
+  if (threadIdx.x == 0) *cnt = (uint32_t)total;
 }
 
 hipError_t launch_topk_filter(const TopkPlan& p, hipStream_t s) {
   dim3 grid(p.n_chunks, p.rows);
-  topk_filter_kernel<<<grid, 256, 0, s>>>(p);
+  topk_filter_kernel<<<grid, kFiltThreads, 0, s>>>(p);
   return hipGetLastError();
 }
 
@@ -219,10 +252,14 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkPlan p) {
   }
   if (k_eff <= 0) return;
 
-  const uint32_t* g = p.hist + (int64_t)r * kHistStride;
-  const uint32_t b1 = g[kHistBstar];
-  int above = (int)g[kHistAbove];
+  const uint32_t b1 = p.bstar[2 * r];
+  int above = (int)p.bstar[2 * r + 1];
+  const int wid = tid >> 6;
+  const int lane = tid & 63;
 
+  // level-2 histogram (bits [19:8] of the keys in bin b1), counted while
+  // the candidates are staged
+  for (int i = tid; i < kHistBins; i += kSelThreads) hs[i] = 0u;
   // chunk offsets
   const uint32_t* cc = p.chunk_cnt + (int64_t)r * p.n_chunks;
   int M = 0;
@@ -242,25 +279,28 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkPlan p) {
     int c = find_chunk(excl, nch, q);
     return (int64_t)c * kTopkChunk + (q - excl[c]);
   };
-  // stage the candidates (in index order) in LDS when they fit
+  // stage the candidates (in index order) in LDS when they fit: wave w
+  // copies chunks w, w + 16, ...
   const bool inlds = M <= kSelCap;
   if (inlds) {
+    for (int c = wid; c < nch; c += kSelThreads / 64) {
+      const int cnt = (c + 1 < nch ? excl[c + 1] : M) - excl[c];
+      const int dst = excl[c];
+      for (int i = lane; i < cnt; i += 64) {
+        const uint32_t key = ck[(int64_t)c * kTopkChunk + i];
+        ckey_s[dst + i] = key;
+        cidx_s[dst + i] = ci[(int64_t)c * kTopkChunk + i];
+        if ((key >> 20) == b1) atomicAdd(&hs[(key >> 8) & 0xFFFu], 1u);
+      }
+    }
+  } else {
     for (int q = tid; q < M; q += kSelThreads) {
-      const int64_t o = cand_off(q);
-      ckey_s[q] = ck[o];
-      cidx_s[q] = ci[o];
+      const uint32_t key = ck[cand_off(q)];
+      if ((key >> 20) == b1) atomicAdd(&hs[(key >> 8) & 0xFFFu], 1u);
     }
   }
   auto key_at = [&](int q) -> uint32_t { return inlds ? ckey_s[q] : ck[cand_off(q)]; };
   auto idx_at = [&](int q) -> int32_t { return inlds ? cidx_s[q] : ci[cand_off(q)]; };
-
-  // level 2: bits [19:8] of the keys in bin b1
-  for (int i = tid; i < kHistBins; i += kSelThreads) hs[i] = 0u;
-  __syncthreads();
-  for (int q = tid; q < M; q += kSelThreads) {
-    uint32_t key = key_at(q);
-    if ((key >> 20) == b1) atomicAdd(&hs[(key >> 8) & 0xFFFu], 1u);
-  }
   if (tid == 0) { res[0] = 0; res[1] = 0; }
   __syncthreads();
   find_bin_from_top<kSelThreads>(hs, kHistBins, k_eff - above, scan_lds, res);
