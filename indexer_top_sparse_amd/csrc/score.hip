@@ -45,10 +45,15 @@ __device__ __forceinline__ int valid_len(const int32_t* seq_lens, int b,
 // DOT: s_t = sum_h q_h . k_t  (= q_bar . k_t, q_bar = sum_h q_h formed once
 // in fp64 and rounded to fp32), optional max over 64-token blocks.
 //
-// Layout: LPR = 16 lanes cover one 256-byte bf16 row (32 lanes for fp32);
-// a wave loads RPI = 64/LPR rows per instruction, fully coalesced.  Each
-// lane keeps partial dots of LPR rows and a reduce-scatter butterfly over
-// the LPR lanes leaves one finished token score per lane.
+// A wave streams 64-token tiles with fully coalesced non-temporal 16-byte
+// loads: LPR lanes cover one row (16 for 256-byte bf16 rows, 32 for 512-byte
+// fp32 rows), so load j of a tile holds rows RPI j .. RPI j + RPI - 1
+// (RPI = 64 / LPR) and a lane always reads the same 16-byte column chunk c,
+// whose q_bar values it keeps in registers.  After the LPR loads a lane
+// holds LPR partial dots (one per load); a reduce-scatter over the LPR lanes
+// of a row -- exchanges by DPP row rotate / mirror / quad permutes and one
+// 16-lane swap, no LDS -- leaves lane l with the full dot of tile row
+// RPI (l % LPR) + l / LPR.  bf16 tiles are double buffered in registers.
 // ========================================================================
 template <typename T>
 struct DotTraits;
@@ -56,39 +61,96 @@ template <>
 struct DotTraits<float> {
   static constexpr int kLPR = 32;  // 128 fp32 = 512 B = 32 x 16 B
   static constexpr int kPerLoad = 4;
+  static constexpr int kStages = 1;
 };
 template <>
 struct DotTraits<uint16_t> {
   static constexpr int kLPR = 16;  // 128 bf16 = 256 B = 16 x 16 B
   static constexpr int kPerLoad = 8;
+  static constexpr int kStages = 2;
 };
 
-__device__ __forceinline__ void load_elems(const float* p, float* x) {
-  f32x4 v = *(const f32x4*)p;
-  x[0] = v[0]; x[1] = v[1]; x[2] = v[2]; x[3] = v[3];
+__device__ __forceinline__ void unpack16(const u32x4& v, float* x) {  // 4 fp32
+  x[0] = __uint_as_float(v[0]); x[1] = __uint_as_float(v[1]);
+  x[2] = __uint_as_float(v[2]); x[3] = __uint_as_float(v[3]);
 }
-__device__ __forceinline__ void load_elems(const uint16_t* p, float* x) {
-  uint4 v = *(const uint4*)p;
-  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+__device__ __forceinline__ void unpack16_bf16(const u32x4& v, float* x) {  // 8 bf16
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    x[2 * i] = __uint_as_float(w[i] << 16);
-    x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    x[2 * i] = __uint_as_float(v[i] << 16);
+    x[2 * i + 1] = __uint_as_float(v[i] & 0xFFFF0000u);
   }
 }
 
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float lane_xor16(float v) {  // value of lane l ^ 16
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float((threadIdx.x & 16) ? r[0] : r[1]);
+}
+
+// One halving step of the reduce-scatter over N partials: partner lanes
+// (given by XCH) exchange halves; a lane with `up` keeps the upper half.
+template <int N, typename F>
+__device__ __forceinline__ void rs_step(float* p, bool up, F xch) {
+#pragma unroll
+  for (int i = 0; i < N / 2; ++i) {
+    const float keep = up ? p[i + N / 2] : p[i];
+    const float send = up ? p[i] : p[i + N / 2];
+    p[i] = keep + xch(send);
+  }
+}
+
+template <int LPR>
+__device__ __forceinline__ float reduce_scatter(float (&p)[LPR], int lane) {
+  float* q = p;
+  if constexpr (LPR == 32) rs_step<32>(q, lane & 16, [](float v) { return lane_xor16(v); });
+  rs_step<16>(q, lane & 8, [](float v) { return dpp_mov<0x128>(v); });  // row_ror:8 = lane ^ 8
+  rs_step<8>(q, lane & 4, [](float v) { return dpp_mov<0x141>(v); });   // half-row mirror
+  rs_step<4>(q, lane & 2, [](float v) { return dpp_mov<0x4E>(v); });    // lane ^ 2
+  rs_step<2>(q, lane & 1, [](float v) { return dpp_mov<0xB1>(v); });    // lane ^ 1
+  return q[0];
+}
+
+__device__ __forceinline__ float wave_max(float m) {
+  m = fmaxf(m, dpp_mov<0xB1>(m));
+  m = fmaxf(m, dpp_mov<0x4E>(m));
+  m = fmaxf(m, dpp_mov<0x141>(m));
+  m = fmaxf(m, dpp_mov<0x128>(m));
+  m = fmaxf(m, lane_xor16(m));
+  m = fmaxf(m, swap_halves(m));
+  return m;
+}
+
 constexpr int kDotThreads = 256;
-constexpr int kDotTokensPerWG = 2048;
-static_assert(kDotTokensPerWG <= kHistPartMax, "histogram part overflow");
+constexpr int kDotWaves = kDotThreads / kWave;
+constexpr int kDotTile = 64;                       // tokens per wave tile
+constexpr int kDotRound = kDotWaves * kDotTile;    // tokens per workgroup round
+constexpr int kDotMaxRounds = kHistPartMax / kDotRound;
+
+// Rounds per workgroup: about 512 workgroups in all, within one histogram
+// part's capacity.
+int dot_rounds(const sparse_index_args& a) {
+  const int64_t rounds_total = (int64_t)a.batch * ((a.n + kDotRound - 1) / kDotRound);
+  int64_t r = (rounds_total + 511) / 512;
+  return (int)std::min<int64_t>(std::max<int64_t>(r, 1), kDotMaxRounds);
+}
+int dot_parts(const sparse_index_args& a) {
+  const int span = dot_rounds(a) * kDotRound;
+  return (a.n + span - 1) / span;
+}
 
 template <typename T, int BLOCK>
 __global__ __launch_bounds__(kDotThreads) void score_dot_kernel(
-    sparse_index_args a, float* __restrict__ scores, uint32_t* hist,
-    int n_units) {
+    sparse_index_args a, float* __restrict__ scores, uint32_t* hist, int n_units,
+    int rounds) {
   constexpr int LPR = DotTraits<T>::kLPR;
   constexpr int PL = DotTraits<T>::kPerLoad;
-  constexpr int RPI = kWave / LPR;        // rows per load instruction
-  constexpr int BATCH = LPR * RPI;        // = 64 tokens per wave batch
+  constexpr int RPI = kWave / LPR;  // rows per load instruction
+  constexpr int NS = DotTraits<T>::kStages;
+  static_assert(BLOCK == 1 || BLOCK == kDotTile, "block = 1 or one tile");
   __shared__ float qbar_s[128];
   __shared__ uint32_t hist_s[kHistBins];
   LdsHist lh{hist_s};
@@ -99,12 +161,10 @@ __global__ __launch_bounds__(kDotThreads) void score_dot_kernel(
   const int n = a.n;
   const int valid = valid_len(a.seq_lens, b, n);
 
-  if (hist) lh.clear(kDotThreads);
   if (threadIdx.x < 128) {
     double acc = 0.0;
     for (int h = 0; h < a.n_heads; ++h) {
-      const T* qh = (const T*)a.q + (int64_t)b * a.q_stride_b +
-                    (int64_t)h * a.q_stride_h;
+      const T* qh = (const T*)a.q + (int64_t)b * a.q_stride_b + (int64_t)h * a.q_stride_h;
       float x;
       if constexpr (sizeof(T) == 4) x = qh[threadIdx.x];
       else x = bf16_bits_to_f32(qh[threadIdx.x]);
@@ -112,64 +172,71 @@ __global__ __launch_bounds__(kDotThreads) void score_dot_kernel(
     }
     qbar_s[threadIdx.x] = (float)acc;
   }
-  __syncthreads();
+  if (hist) lh.clear(kDotThreads);  // (ends with a barrier)
+  else __syncthreads();
 
-  const int j = lane % LPR;   // 16-byte chunk of the row this lane reads
-  const int g = lane / LPR;   // row within a load instruction
+  const int c = lane % LPR;  // the 16-byte column chunk this lane reads
+  const int g = lane / LPR;  // row within a load instruction
   float qv[PL];
 #pragma unroll
-  for (int e = 0; e < PL; ++e) qv[e] = qbar_s[j * PL + e];
+  for (int e = 0; e < PL; ++e) qv[e] = qbar_s[c * PL + e];
 
-  const T* kb = (const T*)a.keys + (int64_t)b * a.k_stride_b;
-  const int t_begin = blockIdx.x * kDotTokensPerWG;
-  const int t_end = min(t_begin + kDotTokensPerWG, n);
+  const char* kb = (const char*)a.keys + (int64_t)b * a.k_stride_b * (int64_t)sizeof(T);
+  const int64_t rstride = a.k_stride_t * (int64_t)sizeof(T);
+  const int span0 = blockIdx.x * rounds * kDotRound;
   float* srow = scores + (int64_t)b * n_units;
 
-  for (int base = t_begin + wid * BATCH; base < t_end;
-       base += BATCH * (kDotThreads / kWave)) {
+  struct Tile { u32x4 k[LPR]; };
+  auto tile_base = [&](int r) { return span0 + (r * kDotWaves + wid) * kDotTile; };
+  auto issue = [&](Tile& tl, int r) __attribute__((always_inline)) {
+    const int tb = tile_base(r);
+#pragma unroll
+    for (int j = 0; j < LPR; ++j) {
+      int t = tb + RPI * j + g;
+      t = t < n ? t : n - 1;
+      tl.k[j] = __builtin_nontemporal_load((gptr<const u32x4>)(kb + t * rstride + 16 * c));
+    }
+  };
+  auto consume = [&](const Tile& tl, int r) __attribute__((always_inline)) {
+    const int tb = tile_base(r);
+    if (tb >= n) return;  // whole tile past the keys (uniform)
     float part[LPR];
 #pragma unroll
-    for (int i = 0; i < LPR; ++i) {
-      int t = base + i * RPI + g;
-      int tc = t < n ? t : n - 1;
+    for (int j = 0; j < LPR; ++j) {
       float x[PL];
-      load_elems(kb + (int64_t)tc * a.k_stride_t + j * PL, x);
+      if constexpr (sizeof(T) == 4) unpack16(tl.k[j], x);
+      else unpack16_bf16(tl.k[j], x);
       float acc = 0.f;
 #pragma unroll
       for (int e = 0; e < PL; ++e) acc = fmaf(qv[e], x[e], acc);
-      part[i] = acc;
+      part[j] = acc;
     }
-    // reduce-scatter over the LPR lanes of a row group
-#pragma unroll
-    for (int m = LPR / 2; m >= 1; m >>= 1) {
-#pragma unroll
-      for (int i = 0; i < m; ++i) {
-        // lanes with (j & m) keep the upper half [i + m], others the lower
-        float send = (j & m) ? part[i] : part[i + m];
-        float keep = (j & m) ? part[i + m] : part[i];
-        float recv = __shfl_xor(send, m, 64);
-        part[i] = keep + recv;
-      }
-    }
-    // lane holds token base + j*RPI + g
-    const int t = base + j * RPI + g;
-    float s = part[0];
-    if (t >= valid) s = -__builtin_huge_valf();
+    const float dot = reduce_scatter<LPR>(part, lane);
+    const int t = tb + RPI * c + g;
+    const float sc = t < valid ? dot : -__builtin_huge_valf();
     if constexpr (BLOCK == 1) {
       if (t < n) {
-        srow[t] = s;
-        if (hist && t < valid) lh.add(s);
+        srow[t] = sc;
+        if (hist && t < valid) lh.add(sc);
       }
     } else {
-      // BATCH == BLOCK == 64: one block per wave batch
-      float m = s;
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-      const int u = base / BLOCK;
+      const float m = wave_max(sc);
+      const int u = tb / BLOCK;
       if (lane == 0 && u < n_units) {
         srow[u] = m;
-        if (hist && base < valid) lh.add(m);
+        if (hist && tb < valid) lh.add(m);
       }
+    }
+  };
+
+  Tile buf[NS];
+#pragma unroll
+  for (int st = 0; st < NS; ++st) issue(buf[st], st);
+  for (int r = 0; r < rounds; r += NS) {
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+      if (r + st < rounds) consume(buf[st], r + st);
+      if (r + st + NS < rounds) issue(buf[st], r + st + NS);
     }
   }
   if (hist) {
@@ -180,17 +247,18 @@ __global__ __launch_bounds__(kDotThreads) void score_dot_kernel(
 
 hipError_t launch_score_dot(const ScorePlan& p, hipStream_t s) {
   const sparse_index_args& a = *p.a;
-  dim3 grid((a.n + kDotTokensPerWG - 1) / kDotTokensPerWG, a.batch);
+  const int rounds = dot_rounds(a);
+  dim3 grid(dot_parts(a), a.batch);
   if (a.k_dtype == SPARSE_F32) {
     if (a.block_size == 1)
-      score_dot_kernel<float, 1><<<grid, kDotThreads, 0, s>>>(a, p.scores, p.hist, p.n_units);
+      score_dot_kernel<float, 1><<<grid, kDotThreads, 0, s>>>(a, p.scores, p.hist, p.n_units, rounds);
     else
-      score_dot_kernel<float, 64><<<grid, kDotThreads, 0, s>>>(a, p.scores, p.hist, p.n_units);
+      score_dot_kernel<float, 64><<<grid, kDotThreads, 0, s>>>(a, p.scores, p.hist, p.n_units, rounds);
   } else {
     if (a.block_size == 1)
-      score_dot_kernel<uint16_t, 1><<<grid, kDotThreads, 0, s>>>(a, p.scores, p.hist, p.n_units);
+      score_dot_kernel<uint16_t, 1><<<grid, kDotThreads, 0, s>>>(a, p.scores, p.hist, p.n_units, rounds);
     else
-      score_dot_kernel<uint16_t, 64><<<grid, kDotThreads, 0, s>>>(a, p.scores, p.hist, p.n_units);
+      score_dot_kernel<uint16_t, 64><<<grid, kDotThreads, 0, s>>>(a, p.scores, p.hist, p.n_units, rounds);
   }
   return hipGetLastError();
 }
@@ -624,7 +692,7 @@ hipError_t launch_score_bitplane(const ScorePlan& p, hipStream_t s) {
 
 int score_hist_parts(const sparse_index_args& a) {
   switch (a.kind) {
-    case SPARSE_SCORE_DOT: return (a.n + kDotTokensPerWG - 1) / kDotTokensPerWG;
+    case SPARSE_SCORE_DOT: return dot_parts(a);
     case SPARSE_SCORE_LIGHTNING: return lightning_parts(a);
     default: return bitplane_parts(a);
   }
