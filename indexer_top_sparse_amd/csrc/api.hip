@@ -92,8 +92,10 @@ int attn_splits(const sparse_attn_args& a, int k_tokens) {
   if (k_tokens <= 0) return 1;
   int groups, min_tok, target;
   if (a.dtype == SPARSE_F32) {
-    groups = a.n_q_heads;
-    min_tok = 64;
+    // workgroups of up to 8 query heads sharing a KV head
+    const int G = a.n_q_heads / std::max(a.n_kv_heads, 1);
+    groups = a.n_kv_heads * ((G + 7) / 8);
+    min_tok = 16;
     target = 256;
   } else if (a.d_qk == 576) {
     // one 4-wave workgroup per compute unit, 64 heads each

@@ -57,6 +57,18 @@ __device__ __forceinline__ int valid_tokens(const sparse_attn_args& a, int b) {
   return v < 0 ? 0 : (v > a.n ? a.n : v);
 }
 
+// One halving step of a reduce-scatter over N partials: partner lanes
+// (given by xch) exchange halves; a lane with `up` keeps the upper half.
+template <int N, typename F>
+__device__ __forceinline__ void rs_halve(float* p, bool up, F xch) {
+#pragma unroll
+  for (int i = 0; i < N / 2; ++i) {
+    const float keep = up ? p[i + N / 2] : p[i];
+    const float send = up ? p[i] : p[i + N / 2];
+    p[i] = keep + xch(send);
+  }
+}
+
 // Token of selection list position j (-1 if padding or past seq_len).
 __device__ __forceinline__ int sel_token(const int32_t* selrow, int j, int unit,
                                          int valid) {
@@ -67,20 +79,53 @@ __device__ __forceinline__ int sel_token(const int32_t* selrow, int j, int unit,
 }
 
 // =================================================================== fp32
-// One workgroup per (request, query head, split); d <= 256.
+// One workgroup per (request, KV head, group of up to 8 query heads, split);
+// d_qk = d_v = 128.  Each K row is read once for all heads of the group:
+//   QK: a wave takes one token at a time, lane l holds dims 2l, 2l + 1, and a
+//       reduce-scatter over the wave leaves head h's dot in lanes 8h .. 8h+7
+//   softmax per head over the split (waves own heads)
+//   PV: thread (head, column quad) accumulates p_i v_i over the split.
 constexpr int kF32Threads = 256;
+constexpr int kF32Heads = 8;
 constexpr int kF32MaxTok = 2048;
 
+__device__ __forceinline__ float wave_sum_f(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
+  {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x += __uint_as_float((threadIdx.x & 16) ? r[0] : r[1]);
+  }
+  return x + swap_halves(x);
+}
+__device__ __forceinline__ float wave_max_f(float x) {
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false)));
+  {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(x, __uint_as_float((threadIdx.x & 16) ? r[0] : r[1]));
+  }
+  return fmaxf(x, swap_halves(x));
+}
+
 __global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(AttnPlan p) {
-  __shared__ float logit_s[kF32MaxTok];
+  __shared__ float q_s[kF32Heads][128];
+  __shared__ float logit_s[kF32Heads][kF32MaxTok];
   __shared__ int tok_s[kF32MaxTok];
-  __shared__ float red_s[kF32Threads / 64];
-  const int split = blockIdx.x;
-  const int hq = blockIdx.y;
-  const int b = blockIdx.z;
+  __shared__ float ml_s[kF32Heads][2];
   const sparse_attn_args& A = p.a;
+  const int split = blockIdx.x;
   const int G = A.n_q_heads / A.n_kv_heads;
-  const int kvh = hq / G;
+  const int ngrp = (G + kF32Heads - 1) / kF32Heads;
+  const int kvh = blockIdx.y / ngrp;
+  const int hg = blockIdx.y % ngrp;
+  const int h0 = kvh * G + hg * kF32Heads;        // first query head
+  const int nh = min(kF32Heads, G - hg * kF32Heads);
+  const int b = blockIdx.z;
   const int selrow_i = p.sel_heads == 1 ? 0 : kvh;
   const int32_t* selrow = p.sel + ((int64_t)b * p.sel_heads + selrow_i) * p.k;
   const int valid = valid_tokens(A, b);
@@ -88,71 +133,104 @@ __global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(AttnPlan p) {
   const int j0 = split * tps;
   const int j1 = min(j0 + tps, p.k_tokens);
   const int cnt = max(0, j1 - j0);
-  const float* q = (const float*)A.q + (int64_t)b * A.q_stride_b + (int64_t)hq * A.q_stride_h;
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wid = tid >> 6;
   RowAddr ra{A};
-  float lmax = -__builtin_huge_valf();
-  for (int i = tid; i < cnt; i += kF32Threads) {
-    int t = sel_token(selrow, j0 + i, p.sel_unit, valid);
-    tok_s[i] = t;
-    float lg = -__builtin_huge_valf();
-    if (t >= 0) {
-      const float* kr = (const float*)ra.k_row(b, kvh, t, 0, nullptr, 4);
-      float acc = 0.f;
-      for (int d = 0; d < A.d_qk; ++d) acc = fmaf(q[d], kr[d], acc);
-      lg = acc * A.sm_scale;
+  const float* qb = (const float*)A.q + (int64_t)b * A.q_stride_b;
+  for (int i = tid; i < kF32Heads * 128; i += kF32Threads) {
+    const int h = i >> 7;
+    q_s[h][i & 127] = h < nh ? qb[(int64_t)(h0 + h) * A.q_stride_h + (i & 127)] : 0.f;
+  }
+  for (int i = tid; i < cnt; i += kF32Threads) tok_s[i] = sel_token(selrow, j0 + i, p.sel_unit, valid);
+  __syncthreads();
+
+  float qr[kF32Heads][2];
+#pragma unroll
+  for (int h = 0; h < kF32Heads; ++h) {
+    qr[h][0] = q_s[h][2 * lane];
+    qr[h][1] = q_s[h][2 * lane + 1];
+  }
+  const int hl = (lane >> 3) & 7;  // head whose dot this lane ends with
+  constexpr int kU = 4;  // tokens per wave step, their rows loaded together
+  constexpr int kWavesF = kF32Threads / 64;
+  for (int i0 = wid * kU; i0 < cnt; i0 += kWavesF * kU) {
+    f32x2 kvs[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int i = min(i0 + u, cnt - 1);
+      const int t = max(tok_s[i], 0);  // masked positions read token 0's row
+      kvs[u] = *(const f32x2*)((const float*)ra.k_row(b, kvh, t, 0, nullptr, 4) + 2 * lane);
     }
-    logit_s[i] = lg;
-    lmax = fmaxf(lmax, lg);
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+    const int i = i0 + u;
+    const int t = i < cnt ? tok_s[i] : -1;
+    const f32x2 kv = kvs[u];
+    float part[kF32Heads];
+#pragma unroll
+    for (int h = 0; h < kF32Heads; ++h) part[h] = fmaf(qr[h][0], kv[0], qr[h][1] * kv[1]);
+    // reduce-scatter over lane bits 5, 4, 3 (upper half kept when set), then
+    // sum over lane bits 0..2
+    rs_halve<8>(part, lane & 32, [](float v) { return swap_halves(v); });
+    rs_halve<4>(part, lane & 16, [](float v) {
+      auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+      return __uint_as_float((threadIdx.x & 16) ? r[0] : r[1]);
+    });
+    rs_halve<2>(part, lane & 8, [](float v) {
+      return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));
+    });
+    float d = part[0];
+    d += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(d), 0xB1, 0xF, 0xF, false));
+    d += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(d), 0x4E, 0xF, 0xF, false));
+    d += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(d), 0x141, 0xF, 0xF, false));
+    if ((lane & 7) == 0 && hl < nh && i < cnt)
+      logit_s[hl][i] = t >= 0 ? d * A.sm_scale : -__builtin_huge_valf();
+    }
   }
-  for (int off = 32; off >= 1; off >>= 1) lmax = fmaxf(lmax, __shfl_xor(lmax, off, 64));
-  if ((tid & 63) == 0) red_s[tid >> 6] = lmax;
   __syncthreads();
-  float m = red_s[0];
-  for (int w = 1; w < kF32Threads / 64; ++w) m = fmaxf(m, red_s[w]);
-  __syncthreads();
-  float lsum = 0.f;
-  for (int i = tid; i < cnt; i += kF32Threads) {
-    float e = (m == -__builtin_huge_valf()) ? 0.f : __expf(logit_s[i] - m);
-    logit_s[i] = e;
-    lsum += e;
+  for (int h = wid; h < nh; h += kF32Threads / 64) {
+    float m = -__builtin_huge_valf();
+    for (int i = lane; i < cnt; i += 64) m = fmaxf(m, logit_s[h][i]);
+    m = wave_max_f(m);
+    float l = 0.f;
+    for (int i = lane; i < cnt; i += 64) {
+      const float e = m == -__builtin_huge_valf() ? 0.f : __expf(logit_s[h][i] - m);
+      logit_s[h][i] = e;
+      l += e;
+    }
+    l = wave_sum_f(l);
+    if (lane == 0) { ml_s[h][0] = m; ml_s[h][1] = l; }
   }
-  for (int off = 32; off >= 1; off >>= 1) lsum += __shfl_xor(lsum, off, 64);
-  if ((tid & 63) == 0) red_s[tid >> 6] = lsum;
   __syncthreads();
-  float l = 0.f;
-  for (int w = 0; w < kF32Threads / 64; ++w) l += red_s[w];
-  for (int d = tid; d < A.d_v; d += kF32Threads) {
-    float acc = 0.f;
+  const int h = tid >> 5;   // head of this thread's output quad
+  const int qd = tid & 31;  // columns 4 qd .. 4 qd + 3
+  if (h < nh) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
     for (int i = 0; i < cnt; ++i) {
-      int t = tok_s[i];
-      if (t < 0) continue;
-      const float* vr = A.v_cache
-          ? (const float*)ra.v_row(b, kvh, t, 4)
-          : (const float*)ra.k_row(b, kvh, t, 0, nullptr, 4);
-      acc = fmaf(logit_s[i], vr[d], acc);
+      // a masked position has probability 0; it reads token 0's row instead
+      const int t = max(tok_s[i], 0);
+      const float* vr = A.v_cache ? (const float*)ra.v_row(b, kvh, t, 4)
+                                  : (const float*)ra.k_row(b, kvh, t, 0, nullptr, 4);
+      acc += *(const f32x4*)(vr + 4 * qd) * logit_s[h][i];
     }
-    const int64_t oh = (int64_t)b * A.n_q_heads + hq;
+    const float m = ml_s[h][0], l = ml_s[h][1];
+    const int64_t oh = (int64_t)b * A.n_q_heads + h0 + h;
     if (p.splits == 1) {
-      p.out[oh * A.d_v + d] = l > 0.f ? acc / l : 0.f;
+      *(f32x4*)(p.out + oh * 128 + 4 * qd) = l > 0.f ? acc * (1.f / l) : f32x4{0.f, 0.f, 0.f, 0.f};
+      if (qd == 0 && p.lse) p.lse[oh] = l > 0.f ? m + __logf(l) : -__builtin_huge_valf();
     } else {
-      p.part[(oh * p.splits + split) * (A.d_v + 4) + d] = acc;
-    }
-  }
-  if (tid == 0) {
-    const int64_t oh = (int64_t)b * A.n_q_heads + hq;
-    if (p.splits == 1) {
-      if (p.lse) p.lse[oh] = l > 0.f ? m + __logf(l) : -__builtin_huge_valf();
-    } else {
-      float* pp = p.part + (oh * p.splits + split) * (A.d_v + 4);
-      pp[A.d_v] = m;
-      pp[A.d_v + 1] = l;
+      float* pp = p.part + (oh * p.splits + split) * (128 + 4);
+      *(f32x4*)(pp + 4 * qd) = acc;
+      if (qd == 0) { pp[128] = m; pp[129] = l; }
     }
   }
 }
 
 hipError_t launch_attn_f32(const AttnPlan& p, hipStream_t s) {
-  dim3 grid(p.splits, p.a.n_q_heads, p.a.batch);
+  const int G = p.a.n_q_heads / p.a.n_kv_heads;
+  dim3 grid(p.splits, p.a.n_kv_heads * ((G + kF32Heads - 1) / kF32Heads), p.a.batch);
   attn_f32_kernel<<<grid, kF32Threads, 0, s>>>(p);
   return hipGetLastError();
 }
