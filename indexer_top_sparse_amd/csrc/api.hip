@@ -105,7 +105,7 @@ int attn_splits(const sparse_attn_args& a, int k_tokens) {
   } else {
     groups = a.n_kv_heads;
     min_tok = 64;
-    target = 512;
+    target = 1024;
   }
   const int64_t base = (int64_t)std::max(a.batch, 1) * std::max(groups, 1);
   int64_t s = ceil_div(target, base);

@@ -306,25 +306,37 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkPlan p) {
   find_bin_from_top<kSelThreads>(hs, kHistBins, k_eff - above, scan_lds, res);
   const uint32_t b2 = (uint32_t)res[0];
   above += res[1];
+  const uint32_t pre = (b1 << 12) | b2;
+  // When every key of the boundary 24-bit prefix is needed (the usual case),
+  // the prefix itself is the threshold and the last level is skipped.
+  const bool whole_prefix = (int)hs[b2] == k_eff - above;
   __syncthreads();
 
-  // level 3: bits [7:0] of the keys with prefix (b1, b2)
-  const uint32_t pre = (b1 << 12) | b2;
-  for (int i = tid; i < 256; i += kSelThreads) hs[i] = 0u;
-  __syncthreads();
-  for (int q = tid; q < M; q += kSelThreads) {
-    uint32_t key = key_at(q);
-    if ((key >> 8) == pre) atomicAdd(&hs[key & 0xFFu], 1u);
+  uint32_t T;      // threshold on key >> shift
+  int shift;
+  int eq_need, eq_total;
+  if (whole_prefix) {
+    T = pre;
+    shift = 8;
+    eq_need = eq_total = k_eff - above;
+  } else {
+    // level 3: bits [7:0] of the keys with prefix (b1, b2)
+    for (int i = tid; i < 256; i += kSelThreads) hs[i] = 0u;
+    __syncthreads();
+    for (int q = tid; q < M; q += kSelThreads) {
+      uint32_t key = key_at(q);
+      if ((key >> 8) == pre) atomicAdd(&hs[key & 0xFFu], 1u);
+    }
+    if (tid == 0) { res[0] = 0; res[1] = 0; }
+    __syncthreads();
+    find_bin_from_top<kSelThreads>(hs, 256, k_eff - above, scan_lds, res);
+    const uint32_t d3 = (uint32_t)res[0];
+    T = (pre << 8) | d3;
+    shift = 0;
+    eq_need = k_eff - (above + res[1]);
+    eq_total = (int)hs[d3];
+    __syncthreads();
   }
-  if (tid == 0) { res[0] = 0; res[1] = 0; }
-  __syncthreads();
-  find_bin_from_top<kSelThreads>(hs, 256, k_eff - above, scan_lds, res);
-  const uint32_t d3 = (uint32_t)res[0];
-  const uint32_t T = (pre << 8) | d3;
-  const int count_gt = above + res[1];
-  const int eq_need = k_eff - count_gt;
-  const int eq_total = (int)hs[d3];
-  __syncthreads();
 
   // final ordered pass, 4 consecutive candidates per thread per round
   int eq_carry = 0, take_carry = 0;
@@ -338,8 +350,8 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkPlan p) {
     for (int i = 0; i < 4; ++i) {
       const int q = q0 + i;
       key[i] = q < M ? key_at(q) : 0u;
-      gt[i] = (q < M) && key[i] > T;
-      eq[i] = (q < M) && key[i] == T;
+      gt[i] = (q < M) && (key[i] >> shift) > T;
+      eq[i] = (q < M) && (key[i] >> shift) == T;
       n_eq += eq[i];
     }
     int take[4];
