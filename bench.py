@@ -27,9 +27,11 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
 METRIC = "sparse decode steps/s (score+top-k+attn) at 128K ctx; % of HBM peak BW"
 
 
-def algorithmic_bytes(w) -> dict:
-    """Bytes the method must move per step (no score scratch)."""
+def algorithmic_bytes(w, bits=None) -> dict:
+    """Bytes the method must move per step (no score scratch).  bits: the
+    planes read per key of the Fathom scan (default: the bit budget)."""
     B, n, k = w.B, w.n, w.k
+    bits = w.budget if bits is None else bits
     out = {}
     if w.kind == "lightning":
         out["k_index"] = B * n * (w.idx_dim + 4)            # fp8 key + fp32 scale
@@ -44,7 +46,7 @@ def algorithmic_bytes(w) -> dict:
         out["out"] = w.layers * B * w.hq * (w.d_v + 1) * 4
         out["idx_pt"] = B * k * 4
     elif w.kind == "fathom":
-        out["k_index"] = B * w.hkv * (w.budget * n // 8 + w.d_qk * 12)  # planes read + zero/scale/var
+        out["k_index"] = B * w.hkv * (bits * n // 8 + w.d_qk * 12)  # planes read + zero/scale/var
         out["selected_kv"] = B * w.hkv * k * (w.d_qk + w.d_v) * 2
         out["q_w"] = B * w.hq * w.d_qk * 2
         out["out"] = B * w.hq * (w.d_v + 1) * 4
@@ -59,14 +61,15 @@ def algorithmic_bytes(w) -> dict:
     return out
 
 
-def score_kernel_bytes(w) -> int:
+def score_kernel_bytes(w, bits=None) -> int:
     """Algorithmic bytes of one launch of the index-scan kernel."""
+    bits = w.budget if bits is None else bits
     if w.kind == "lightning":
         return w.B * w.n * (w.idx_dim + 4)
     if w.kind == "block":
         return w.B * w.n * w.idx_dim * 2
     if w.kind == "fathom":
-        return w.B * w.hkv * w.budget * w.n // 8
+        return w.B * w.hkv * bits * w.n // 8
     return w.B * w.n * w.d_qk * 4
 
 
@@ -173,7 +176,15 @@ def main() -> int:
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--cpu-requests", type=int, default=4)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--misses", type=int, default=1, help="hot-buffer workloads: 1 = 20%% misses")
+    ap.add_argument("--misses", type=int, default=1,
+                    help="hot-buffer workloads: 1 = the workload's miss rate, 0 = none")
+    ap.add_argument("--miss-rate", type=float, default=None,
+                    help="hot-buffer workloads: this fixed miss rate (e.g. 0.4)")
+    ap.add_argument("--fixed-depth", type=int, default=None, metavar="BITS",
+                    help="Fathom workloads: a fixed allocation of BITS planes per key "
+                         "(the same for every query) instead of the water-filling")
+    ap.add_argument("--host-planes", action="store_true",
+                    help="Fathom workloads: bit planes read in place from pinned host memory")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run the known-size copy that hardware byte counters are scaled by")
     args = ap.parse_args()
@@ -196,6 +207,8 @@ def main() -> int:
 
     isa.lib()  # fail loudly if the HIP library is missing
     w = synth.get(args.config)
+    miss_rate = (args.miss_rate if args.miss_rate is not None
+                 else (w.miss_rate if args.misses else 0.0))
     dev = "cuda"
     print(f"[bench] generating inputs for {w.name}", file=sys.stderr, flush=True)
     sets = []
@@ -204,11 +217,15 @@ def main() -> int:
     for s in range(1 if w.hot else 2):
         ws = w.with_(seed=w.seed + 100 * s)
         inp = synth.make_inputs(ws, dev)
+        if w.kind == "fathom" and args.fixed_depth is not None:
+            inp["depth_in"] = synth.fixed_depths(ws, args.fixed_depth, dev)
+        if w.kind == "fathom" and args.host_planes:
+            inp["planes"] = synth.pinned_copy(inp["planes"])
         hot = None
         if w.hot:
             # the selection the step will make decides which rows are hot
             sel = _selection_for_hot(inp, ws, dev)
-            hw = ws.with_(miss_rate=w.miss_rate if args.misses else 0.0)
+            hw = ws.with_(miss_rate=miss_rate)
             hot = build_hot_buffer(dict(inp, workload=hw), sel, dev)
         sets.append((inp, StepRunner(inp, hot=hot)))
     torch.cuda.synchronize()
@@ -260,11 +277,12 @@ def main() -> int:
         e1.record(stream)
     torch.cuda.synchronize()
     score_ms = sum(e0.elapsed_time(e1) for e0, e1 in evs) / reps
-    kb = score_kernel_bytes(w)
+    bits = args.fixed_depth if (w.kind == "fathom" and args.fixed_depth is not None) else None
+    kb = score_kernel_bytes(w, bits)
     achieved = kb / (score_ms * 1e-3) / 1e9
     traffic = profiled_traffic(w)
 
-    ab = algorithmic_bytes(w)
+    ab = algorithmic_bytes(w, bits)
     line = {
         "metric": METRIC,
         "value": round(steps_s, 2),
@@ -282,7 +300,8 @@ def main() -> int:
                    "index_heads": w.idx_heads, "attn_heads": w.hq, "kv_heads": w.hkv,
                    "d_qk": w.d_qk, "d_v": w.d_v, "page": w.page, "block": w.block,
                    "bit_budget": w.budget, "hot_tokens": w.hot,
-                   "miss_rate": (w.miss_rate if args.misses else 0.0) if w.hot else None,
+                   "miss_rate": miss_rate if w.hot else None,
+                   "fixed_depth_bits": bits, "host_planes": bool(args.host_planes and w.kind == "fathom"),
                    "graph": not args.no_graph},
         "step_bytes": ab["total"],
         "step_GBps": round(ab["total"] / (ms * 1e-3) / 1e9, 1),
@@ -296,8 +315,44 @@ def main() -> int:
     if not args.no_cpu and w.kind == "lightning" and not w.hot:
         print("[bench] timing the oracle on a sample", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(w, sets[0][0], args.cpu_requests)
+    line["append"] = time_append(w, sets[-1][1], stream)
     print(json.dumps(line), flush=True)
     return 0
+
+
+def time_append(w, r, stream) -> dict:
+    """The decode-side append of one new token per request (index entry and
+    KV rows) into the last input set, timed with HIP events (last, since it
+    changes that set's inputs)."""
+    import torch
+    import indexer_top_sparse_amd as isa
+
+    dev = r.topk.device
+    g = torch.Generator(device=dev)
+    g.manual_seed(w.seed * 1000 + 99)
+    pos = torch.tensor([min(w.valid(b), w.n - 1) for b in range(w.B)], dtype=torch.int32,
+                       device=dev)
+    aa, _ = r.layer_args[0]
+    kd = w.idx_dim if w.kind in ("lightning", "block") else w.d_qk
+    key_shape = (w.B, w.hkv, kd) if w.kind == "fathom" else (w.B, kd)
+    key_new = torch.randn(key_shape, generator=g, device=dev)
+    kvh = 1 if w.kind == "lightning" else w.hkv
+    cdt = torch.float32 if w.dtype == "f32" else torch.bfloat16
+    k_new = torch.randn((w.B, kvh, w.d_qk), generator=g, device=dev).to(cdt)
+    v_new = None
+    if aa.c.v_cache:
+        v_new = torch.randn((w.B, kvh, w.d_v), generator=g, device=dev).to(cdt)
+    reps = 20
+    for _ in range(3):
+        isa.sparse_append_token(r.ia, aa, pos, key_new, k_new, v_new, stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        isa.sparse_append_token(r.ia, aa, pos, key_new, k_new, v_new, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return {"us_per_call": round(e0.elapsed_time(e1) / reps * 1e3, 2), "tokens": w.B}
 
 
 def _selection_for_hot(inp, w, dev):

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define SPARSE_ABI_VERSION 1
+#define SPARSE_ABI_VERSION 2
 
 enum sparse_status {
   SPARSE_OK = 0,
@@ -122,8 +122,15 @@ typedef struct sparse_index_args {
                                bit i of word w is token 32w + i            */
   const float* chan_zero;   /* [B][Hkv][D] quantizer zero (channel min)   */
   const float* chan_scale;  /* [B][Hkv][D] 4-bit cell width ((max-min)/16) */
-  const float* chan_var;    /* [B][Hkv][D] channel variance var_c          */
+  const float* chan_var;    /* [B][Hkv][D] channel variance var_c (unused
+                               with depth_in)                              */
   int32_t bit_budget;       /* bits read per key per KV head, 0..4*D      */
+  /* BITPLANE, nullable: [B][Hkv][D] int8 read depths t_c given by the
+   * caller (values clamped to 0..4), in place of the reverse water-filling
+   * over chan_var and bit_budget -- a fixed allocation, e.g. the same
+   * prefix for every query.  The scan, its score constant and the plane
+   * weights follow these depths exactly as they follow computed ones.     */
+  const int8_t* depth_in;
 } sparse_index_args;
 
 /* Arguments of the sparse attention. */
@@ -195,7 +202,8 @@ int sparse_topk_workspace_size(int32_t rows, int32_t n_units, int32_t k,
  * query heads in float64, importance imp_c = (q_bar_c * q_bar_c) * var_c,
  * gains imp_c * 4^-j for planes j = 0..3, the bit_budget largest gains are
  * taken (ties: lower channel, then lower plane); t_c counts the taken planes
- * of channel c.  depth_out: [B][Hkv][D] int8.  Only kind BITPLANE. */
+ * of channel c.  With depth_in set, depth_out receives those depths
+ * (clamped to 0..4).  depth_out: [B][Hkv][D] int8.  Only kind BITPLANE. */
 int sparse_read_depth(const sparse_index_args* ia, int8_t* depth_out,
                       void* stream);
 
@@ -239,6 +247,36 @@ int sparse_gather_attn_decode(const sparse_attn_args* aa, const int32_t* sel,
 int sparse_decode_step(const sparse_index_args* ia, const sparse_attn_args* aa,
                        int32_t k, int32_t* topk_out, float* out, float* lse,
                        void* ws, size_t ws_bytes, void* stream);
+
+/* Decode-side append: after a step, the new token of each request joins
+ * the history the next step reads -- [XM] KV-lifecycle list (generated KV
+ * is appended to the history), [MM] the decode path's sparse-KV store (the
+ * step's KV and index entries are written once; a repeated write is
+ * idempotent), [FA] abstract (the 4-bit K is stored channel-major as bit
+ * planes).  pos: [B] int32, the token position of the new entry; a request
+ * whose pos is outside 0..n-1 is skipped.  Either struct may be NULL.
+ *   aa (attention history): k_new [B][Hkv][d_qk] (aa->dtype) is written as
+ *     the K row (the latent row when v_cache is NULL) of token pos[b] of
+ *     each KV head, at the address the attention reads it from (contiguous,
+ *     paged, or -- with a hot buffer -- the pinned host KV through host_kv;
+ *     the hot buffer itself is not changed); v_new [B][Hkv][d_v] is the V
+ *     row when v_cache is set (NULL otherwise).
+ *   ia (index): index_key_new holds the new, unquantised key in fp32:
+ *     DOT        [B][D]: stored in the keys' dtype (bf16: round to nearest
+ *                even); block scores of a partly filled block change.
+ *     LIGHTNING  [B][D]: scale = max|k| / 448 in fp32 (1 for an all-zero
+ *                key) into k_scale, and each byte the OCP E4M3FN value
+ *                nearest to clamp(k / scale, -448, 448) (fp32 division;
+ *                ties to the even code).
+ *     BITPLANE   [B][Hkv][D]: code = min(max(floor((k - zero) / cell), 0),
+ *                15) in fp64 against chan_zero / chan_scale (0 when cell
+ *                is 0); bit (3 - j) of the code goes to bit pos % 32 of word
+ *                pos / 32 of plane j.  The quantizer is not refitted.
+ * Only the head_dim 128 index layouts are written; q, head_w, chan_var and
+ * seq_lens are not used.  Nothing else is read or written. */
+int sparse_append_token(const sparse_index_args* ia, const sparse_attn_args* aa,
+                        const int32_t* pos, const float* index_key_new,
+                        const void* k_new, const void* v_new, void* stream);
 
 /* Device-visible address of pinned host memory allocated with
  * hipHostMalloc (e.g. a pinned torch tensor); used for host_kv. */

@@ -36,6 +36,7 @@ class IndexArgs(ctypes.Structure):
         ("block_size", _i32),
         ("n_kv_heads", _i32), ("planes", _vp), ("chan_zero", _vp),
         ("chan_scale", _vp), ("chan_var", _vp), ("bit_budget", _i32),
+        ("depth_in", _vp),
     ]
 
 
@@ -90,10 +91,11 @@ def lib() -> ctypes.CDLL:
         L.sparse_decode_step.argtypes = [P(IndexArgs), P(AttnArgs), _i32, _vp, _vp,
                                          _vp, _vp, ctypes.c_size_t, _vp]
         L.sparse_host_device_pointer.argtypes = [_vp, P(_vp)]
+        L.sparse_append_token.argtypes = [P(IndexArgs), P(AttnArgs), _vp, _vp, _vp, _vp, _vp]
         for f in ("sparse_workspace_size", "sparse_topk_workspace_size",
                   "sparse_read_depth", "sparse_index_score", "sparse_topk",
                   "sparse_gather_attn_decode", "sparse_decode_step",
-                  "sparse_host_device_pointer"):
+                  "sparse_host_device_pointer", "sparse_append_token"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -175,12 +177,15 @@ def lightning_index_args(q: torch.Tensor, head_w: torch.Tensor, k8: torch.Tensor
 
 def bitplane_index_args(q: torch.Tensor, planes: torch.Tensor,
                         chan_zero: torch.Tensor, chan_scale: torch.Tensor,
-                        chan_var: torch.Tensor, bit_budget: int, n: int,
-                        seq_lens: torch.Tensor | None = None) -> _Holder:
+                        chan_var: torch.Tensor | None, bit_budget: int, n: int,
+                        seq_lens: torch.Tensor | None = None,
+                        depth_in: torch.Tensor | None = None) -> _Holder:
     """Fathom scan.  q [B][Hq][D] bf16, planes [B][Hkv][D][4][ceil(n/32)]
-    (int32/uint32 bit words), chan_* [B][Hkv][D] fp32."""
-    for t in (planes, chan_zero, chan_scale, chan_var):
-        if not t.is_contiguous():
+    (int32/uint32 bit words; a pinned host tensor is read in place through
+    its device alias), chan_* [B][Hkv][D] fp32, depth_in (optional) [B][Hkv][D]
+    int8 fixed read depths."""
+    for t in (planes, chan_zero, chan_scale, chan_var, depth_in):
+        if t is not None and not t.is_contiguous():
             raise ValueError("planes and channel tensors must be contiguous")
     a = IndexArgs()
     a.kind = SCORE_BITPLANE
@@ -191,10 +196,12 @@ def bitplane_index_args(q: torch.Tensor, planes: torch.Tensor,
     a.q_stride_b, a.q_stride_h = q.stride(0), q.stride(1)
     a.block_size = 1
     a.n_kv_heads = planes.shape[1]
-    a.planes, a.chan_zero = _p(planes), _p(chan_zero)
+    a.planes = host_device_pointer(planes) if planes.device.type == "cpu" else _p(planes)
+    a.chan_zero = _p(chan_zero)
     a.chan_scale, a.chan_var = _p(chan_scale), _p(chan_var)
     a.bit_budget = bit_budget
-    return _Holder(a, q, planes, chan_zero, chan_scale, chan_var, seq_lens)
+    a.depth_in = _p(depth_in)
+    return _Holder(a, q, planes, chan_zero, chan_scale, chan_var, seq_lens, depth_in)
 
 
 def attn_args(q: torch.Tensor, k_cache: torch.Tensor | None,
@@ -314,9 +321,25 @@ def sparse_decode_step(ia: _Holder, aa: _Holder, k: int, topk_out: torch.Tensor,
                                     _p(lse), _p(ws), ws.numel(), _stream(stream)))
 
 
+def sparse_append_token(ia: _Holder | None, aa: _Holder | None, pos: torch.Tensor,
+                        index_key_new: torch.Tensor | None, k_new: torch.Tensor | None,
+                        v_new: torch.Tensor | None = None, stream=None) -> None:
+    """Append each request's new token (at position pos[b]) to the structures
+    the next step reads: the KV rows of `aa`'s layout (k_new [B][Hkv][d_qk],
+    v_new [B][Hkv][d_v] when V is separate) and the index entry of `ia`'s kind
+    from the fp32 key index_key_new ([B][D], or [B][Hkv][D] for bit planes)."""
+    for t in (pos, index_key_new, k_new, v_new):
+        if t is not None and not t.is_contiguous():
+            raise ValueError("append inputs must be contiguous")
+    _check(lib().sparse_append_token(ia.ref() if ia is not None else None,
+                                     aa.ref() if aa is not None else None,
+                                     _p(pos), _p(index_key_new), _p(k_new), _p(v_new),
+                                     _stream(stream)))
+
+
 def host_device_pointer(host: torch.Tensor) -> int:
     if not host.is_pinned():
-        raise ValueError("host_kv must be pinned host memory")
+        raise ValueError("host tensor must be pinned host memory")
     dev = ctypes.c_void_p(0)
     _check(lib().sparse_host_device_pointer(_p(host), ctypes.byref(dev)))
     return dev.value

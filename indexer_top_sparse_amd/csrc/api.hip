@@ -169,11 +169,13 @@ int check_index(const sparse_index_args* a) {
           "LIGHTNING n_heads %d (32 or 64)", a->n_heads);
     CHECK(a->head_w && a->k_scale, SPARSE_EINVAL, "head_w / k_scale NULL");
   }
+  CHECK(a->depth_in == nullptr || a->kind == SPARSE_SCORE_BITPLANE, SPARSE_EINVAL,
+        "depth_in is for kind BITPLANE only");
   if (a->kind == SPARSE_SCORE_BITPLANE) {
     CHECK(a->n_kv_heads >= 1 && a->n_heads % a->n_kv_heads == 0, SPARSE_EINVAL,
           "n_heads %d not a multiple of n_kv_heads %d", a->n_heads, a->n_kv_heads);
-    CHECK(a->planes && a->chan_zero && a->chan_scale && a->chan_var, SPARSE_EINVAL,
-          "planes / chan_zero / chan_scale / chan_var NULL");
+    CHECK(a->planes && a->chan_zero && a->chan_scale && (a->chan_var || a->depth_in),
+          SPARSE_EINVAL, "planes / chan_zero / chan_scale / chan_var NULL");
     CHECK(a->bit_budget >= 0 && a->bit_budget <= 4 * a->head_dim, SPARSE_EINVAL,
           "bit_budget %d outside 0..%d", a->bit_budget, 4 * a->head_dim);
   }
@@ -477,6 +479,71 @@ int sparse_decode_step(const sparse_index_args* ia, const sparse_attn_args* aa, 
   rc = run_topk(tp, true, s);
   if (rc) return rc;
   return run_attn(*aa, topk_out, sel_heads, k, unit, out, lse, w, L.end, s);
+}
+
+int sparse_append_token(const sparse_index_args* ia, const sparse_attn_args* aa,
+                        const int32_t* pos, const float* index_key_new, const void* k_new,
+                        const void* v_new, void* stream) {
+  CHECK(ia || aa, SPARSE_EINVAL, "both args NULL");
+  int batch = -1;
+  if (ia) {
+    CHECK(ia->kind >= 0 && ia->kind <= 2, SPARSE_EINVAL, "unknown score kind %d", ia->kind);
+    CHECK(ia->batch >= 0 && ia->n >= 0, SPARSE_EINVAL, "negative batch or n");
+    CHECK(ia->head_dim == 128, SPARSE_EUNSUPPORTED, "head_dim %d (only 128)", ia->head_dim);
+    batch = ia->batch;
+    if (ia->batch > 0) {
+      CHECK(index_key_new, SPARSE_EINVAL, "index_key_new NULL");
+      if (ia->kind == SPARSE_SCORE_DOT) {
+        CHECK(ia->keys && (ia->k_dtype == SPARSE_F32 || ia->k_dtype == SPARSE_BF16),
+              SPARSE_EINVAL, "DOT keys NULL or not f32/bf16");
+      } else if (ia->kind == SPARSE_SCORE_LIGHTNING) {
+        CHECK(ia->keys && ia->k_scale && ia->k_dtype == SPARSE_E4M3FN, SPARSE_EINVAL,
+              "LIGHTNING keys / k_scale NULL or keys not e4m3fn");
+        CHECK(ia->k_stride_t % 2 == 0 && ia->k_stride_b % 2 == 0 &&
+                  ((uintptr_t)ia->keys & 1u) == 0,
+              SPARSE_EINVAL, "LIGHTNING key rows must be 2-byte aligned");
+      } else {
+        CHECK(ia->n_kv_heads >= 1 && ia->planes && ia->chan_zero && ia->chan_scale,
+              SPARSE_EINVAL, "BITPLANE planes / chan_zero / chan_scale NULL");
+      }
+    }
+  }
+  if (aa) {
+    CHECK(aa->batch >= 0 && aa->n >= 0 && aa->n_kv_heads >= 1, SPARSE_EINVAL,
+          "attention batch / n / n_kv_heads");
+    CHECK(batch < 0 || batch == aa->batch, SPARSE_EINVAL, "batch differs between args");
+    batch = aa->batch;
+    CHECK(aa->dtype == SPARSE_F32 || aa->dtype == SPARSE_BF16, SPARSE_EUNSUPPORTED,
+          "attention dtype %d", aa->dtype);
+    const int64_t e = esize(aa->dtype);
+    CHECK((aa->d_qk * e) % 16 == 0 && (aa->v_cache == nullptr || (aa->d_v * e) % 16 == 0),
+          SPARSE_EUNSUPPORTED, "row widths must be multiples of 16 bytes");
+    if (aa->batch > 0) {
+      CHECK(k_new && aligned16(k_new), SPARSE_EINVAL, "k_new NULL or not 16-byte aligned");
+      CHECK(aa->v_cache == nullptr || (v_new && aligned16(v_new)), SPARSE_EINVAL,
+            "v_new NULL or not 16-byte aligned");
+      if (aa->hot_slot) {
+        CHECK(aa->v_cache == nullptr, SPARSE_EUNSUPPORTED, "hot buffer: latent rows only");
+        CHECK(aa->host_kv && aligned16(aa->host_kv) && (aa->host_stride_t * e) % 16 == 0 &&
+                  (aa->host_stride_b * e) % 16 == 0,
+              SPARSE_EINVAL, "host_kv NULL or misaligned");
+      } else {
+        CHECK(aa->k_cache && aligned16(aa->k_cache), SPARSE_EINVAL,
+              "k_cache NULL or not 16-byte aligned");
+        CHECK(aa->v_cache == nullptr || aligned16(aa->v_cache), SPARSE_EINVAL,
+              "v_cache not 16-byte aligned");
+        CHECK((aa->kv_stride_t * e) % 16 == 0 && (aa->kv_stride_h * e) % 16 == 0 &&
+                  (aa->kv_stride_b * e) % 16 == 0,
+              SPARSE_EINVAL, "KV strides must be multiples of 16 bytes");
+        if (aa->page_table) CHECK(aa->page_size >= 1, SPARSE_EINVAL, "page_size < 1");
+      }
+    }
+  }
+  if (batch == 0) return SPARSE_OK;
+  CHECK(pos, SPARSE_EINVAL, "pos NULL");
+  HIPCHECK(sd::launch_append(ia, aa, pos, index_key_new, k_new, v_new, batch,
+                             (hipStream_t)stream));
+  return SPARSE_OK;
 }
 
 int sparse_host_device_pointer(void* host_ptr, void** dev_ptr) {

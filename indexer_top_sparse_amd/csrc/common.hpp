@@ -178,5 +178,8 @@ hipError_t launch_attn_f32(const AttnPlan& p, hipStream_t s);
 hipError_t launch_attn_bf16(const AttnPlan& p, hipStream_t s);
 hipError_t launch_attn_combine(const AttnPlan& p, hipStream_t s);
 hipError_t launch_miss_fetch(const AttnPlan& p, hipStream_t s);
+hipError_t launch_append(const sparse_index_args* ia, const sparse_attn_args* aa,
+                         const int32_t* pos, const float* key_new, const void* k_new,
+                         const void* v_new, int batch, hipStream_t s);
 
 }  // namespace sd

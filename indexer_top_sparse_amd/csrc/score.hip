@@ -512,12 +512,18 @@ __global__ __launch_bounds__(kDepthThreads) void read_depth_kernel(
     qbar_s[tid] = acc;
   }
   __syncthreads();
-  if (c < D) {
+  if (a.depth_in == nullptr && c < D) {
     double qb = qbar_s[c];
     double imp = __dmul_rn(__dmul_rn(qb, qb), (double)a.chan_var[hd + c]);
     gain_s[tid] = ldexp(imp, -2 * j);
   }
   __syncthreads();
+  if (a.depth_in) {
+    // a fixed allocation from the caller: planes j < t_c of channel c
+    const int tc = c < D ? min(max((int)a.depth_in[hd + c], 0), 4) : 0;
+    taken_s[tid] = j < tc;
+    __syncthreads();
+  } else {
   // Rank every gain in the total order (gain desc, channel asc, plane asc)
   // -- index order tid = 4c + j is (channel, plane) ascending -- with a
   // bitonic sort of (gain, index) pairs: position r of the sorted list holds
@@ -543,6 +549,7 @@ __global__ __launch_bounds__(kDepthThreads) void read_depth_kernel(
     __syncthreads();
     taken_s[id] = tid < a.bit_budget;  // element id has rank tid
     __syncthreads();
+  }
   }
   const int taken = c < D ? taken_s[tid] : 0;
   if (tid < D) {

@@ -3,7 +3,8 @@
 ``StepRunner(inputs)`` takes the tensors of one decode step (keys as in
 ``synth.make_inputs``: q_idx/head_w/k8/k_scale/kv_pool/page_table for the
 lightning kind, q/k_cache/v_cache for the dot kind, q_idx/k_idx/layers for
-the block kind, q/planes/chan_*/k_cache/v_cache for the Fathom kind), builds
+the block kind, q/planes/chan_*/k_cache/v_cache (+ optional depth_in, and
+planes may be pinned host memory) for the Fathom kind), builds
 the argument structs, output buffers and workspace once, and ``run()``
 enqueues one whole step: ``sparse_decode_step`` and, for workloads whose
 later layers reuse the selection, ``sparse_gather_attn_decode`` per extra
@@ -63,7 +64,7 @@ class StepRunner:
         elif w.kind == "fathom":
             self.ia = bitplane_index_args(inp["q"], inp["planes"], inp["chan_zero"],
                                           inp["chan_scale"], inp["chan_var"], w.budget,
-                                          n, seq)
+                                          n, seq, depth_in=inp.get("depth_in"))
             self.layer_args.append((attn_args(inp["q"], inp["k_cache"], inp["v_cache"],
                                               n=n, seq_lens=seq), w.hq))
             self.unit, self.rows = 1, w.hkv

@@ -199,8 +199,9 @@ def block_step(arr: dict, p: dict, sel_in: np.ndarray | None = None,
 def fathom_step(arr: dict, p: dict, requests=None,
                 sel_in: np.ndarray | None = None) -> dict:
     """Fathom scan: per (request, KV head) read depth by reverse
-    water-filling, plane-prefix scores, top-k tokens per KV head, bf16 GQA
-    attention of that head's query group over its own selection."""
+    water-filling (or the fixed depths arr["depth_in"] when given),
+    plane-prefix scores, top-k tokens per KV head, bf16 GQA attention of that
+    head's query group over its own selection."""
     q_all = O.decode_bf16(arr["q"])
     B, Hq, D = q_all.shape
     hkv = arr["codes"].shape[1]
@@ -214,7 +215,10 @@ def fathom_step(arr: dict, p: dict, requests=None,
         for h in range(hkv):
             qbar = O.fathom_group_query(q_all[b, h * G:(h + 1) * G])
             var = O.decode_f32(arr["chan_var"][b, h])
-            t = O.fathom_read_depth(qbar, var, budget)
+            if "depth_in" in arr:  # a fixed allocation given by the caller
+                t = np.clip(arr["depth_in"][b, h].astype(np.int64), 0, 4)
+            else:
+                t = O.fathom_read_depth(qbar, var, budget)
             s = O.score_fathom(qbar, arr["codes"][b, h, :valid],
                                O.decode_f32(arr["chan_zero"][b, h]),
                                O.decode_f32(arr["chan_scale"][b, h]), t)

@@ -9,4 +9,5 @@ benchmark and the smoke check, which feed the same inputs to the HIP library
 and to the CPU oracle.
 """
 from .workloads import WORKLOADS, Workload, get  # noqa: F401
-from .gen import make_inputs, host_view, quantize_4bit, build_hot_buffer  # noqa: F401
+from .gen import (make_inputs, host_view, quantize_4bit, build_hot_buffer,  # noqa: F401
+                  fixed_depths, random_depths, pinned_copy)

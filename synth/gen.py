@@ -257,6 +257,31 @@ def build_hot_buffer(inp: dict, selection: torch.Tensor, device,
             "n_miss": n_miss}
 
 
+def fixed_depths(w: Workload, bits: int, device) -> torch.Tensor:
+    """A fixed read allocation of `bits` bits per key for every (request,
+    KV head): floor(bits / D) planes in every channel and one more in the
+    first bits % D channels.  [B][Hkv][D] int8."""
+    D = w.d_qk
+    base, extra = divmod(bits, D)
+    t = np.full((w.B, w.hkv, D), base, dtype=np.int8)
+    t[:, :, :extra] += 1
+    return torch.from_numpy(t).to(device)
+
+
+def random_depths(w: Workload, device, seed: int = 7) -> torch.Tensor:
+    """Seeded random read depths 0..4, [B][Hkv][D] int8."""
+    rng = np.random.Generator(np.random.PCG64(w.seed * 1000 + seed))
+    t = rng.integers(0, 5, size=(w.B, w.hkv, w.d_qk)).astype(np.int8)
+    return torch.from_numpy(t).to(device)
+
+
+def pinned_copy(t: torch.Tensor) -> torch.Tensor:
+    """A copy of `t` in pinned host memory."""
+    h = torch.empty(t.shape, dtype=t.dtype, pin_memory=True)
+    h.copy_(t)
+    return h
+
+
 def host_view(t: torch.Tensor) -> np.ndarray:
     """A CPU numpy copy; bf16 comes back as uint16 bit patterns."""
     t = t.detach().to("cpu")

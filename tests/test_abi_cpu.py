@@ -29,7 +29,7 @@ def test_header_symbols_exported():
 
 
 def test_version_and_strerror():
-    assert isa.sparse_abi_version() == 1
+    assert isa.sparse_abi_version() == 2
     L = isa.lib()
     assert L.sparse_strerror(0) == b"ok"
     assert L.sparse_strerror(3) == b"workspace too small"
@@ -116,6 +116,18 @@ def test_index_validation_codes():
     a.bit_budget, a.n_heads = 92, 30  # 30 % 8 != 0
     assert L.sparse_index_score(ctypes.byref(a), FAKE, FAKE, 1 << 30, None) == \
         isa.SPARSE_EINVAL
+    # fixed read depths are for the bit-plane scan only
+    a = _lightning()
+    a.depth_in = FAKE
+    assert L.sparse_index_score(ctypes.byref(a), FAKE, None, 0, None) == isa.SPARSE_EINVAL
+    # with fixed depths the variances may be absent; without them they may not
+    a = _lightning()
+    a.kind, a.n_heads, a.n_kv_heads, a.bit_budget = isa.SCORE_BITPLANE, 32, 8, 92
+    a.planes = a.chan_zero = a.chan_scale = FAKE
+    a.chan_var = None
+    assert L.sparse_index_score(ctypes.byref(a), FAKE, FAKE, 1 << 30, None) == \
+        isa.SPARSE_EINVAL
+    assert L.sparse_abi_version() == 2
     # empty batch: nothing to do, nothing launched
     a = _lightning(B=0)
     assert L.sparse_index_score(ctypes.byref(a), None, None, 0, None) == isa.SPARSE_OK
@@ -166,3 +178,23 @@ def test_decode_step_consistency_codes():
     ia, aa = _lightning(B=2), _mla_attn(B=2)
     assert L.sparse_decode_step(ctypes.byref(ia), ctypes.byref(aa), 16, FAKE, FAKE,
                                 None, FAKE, 64, None) == isa.SPARSE_EWORKSPACE
+
+
+def test_append_validation_codes():
+    L = isa.lib()
+    assert L.sparse_append_token(None, None, FAKE, FAKE, FAKE, None, None) == isa.SPARSE_EINVAL
+    a = _lightning()
+    a.head_dim = 64
+    assert L.sparse_append_token(ctypes.byref(a), None, FAKE, FAKE, None, None, None) == \
+        isa.SPARSE_EUNSUPPORTED
+    a = _lightning()
+    assert L.sparse_append_token(ctypes.byref(a), None, None, FAKE, None, None, None) == \
+        isa.SPARSE_EINVAL  # pos NULL
+    assert L.sparse_append_token(ctypes.byref(a), None, FAKE, None, None, None, None) == \
+        isa.SPARSE_EINVAL  # new key NULL
+    a.k_dtype = isa.BF16
+    assert L.sparse_append_token(ctypes.byref(a), None, FAKE, FAKE, None, None, None) == \
+        isa.SPARSE_EINVAL  # lightning keys must be e4m3fn
+    a = _lightning(B=0)
+    assert L.sparse_append_token(ctypes.byref(a), None, None, None, None, None, None) == \
+        isa.SPARSE_OK

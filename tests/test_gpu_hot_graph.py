@@ -1,9 +1,9 @@
 """GPU: hot-buffer miss fetch and HIP-graph replay of whole steps.
 
-* With a 20 % miss rate the step fetches the missing selected rows from
-  pinned host memory; its output must equal the oracle's attention, and be
-  bit-identical to the same step with every selected row hot ("XM-Sparse"
-  blog: fixed miss rates, misses fetched over PCIe into HBM).
+* With a 20 % or a 40 % miss rate the step fetches the missing selected rows
+  from pinned host memory; its output must equal the oracle's attention, and
+  be bit-identical to the same step with every selected row hot
+  ("XM-Sparse" blog: fixed miss rates, misses fetched over PCIe into HBM).
 * A captured step replayed several times, with eager work and
   synchronisation in between, must reproduce the eager result bit for bit
   on every replay.
@@ -22,10 +22,11 @@ from helpers import arrays, oracle_step
 pytestmark = pytest.mark.gpu
 
 
-@pytest.fixture(scope="module")
-def hot_case():
-    w = synth.get("hot_small")
-    print(f"[hot] workload={w.name}", flush=True)
+@pytest.fixture(scope="module", params=[0.2, 0.4])
+def hot_case(request):
+    """The hot-buffer workload at the pages' two miss rates (20 % and 40 %)."""
+    w = synth.get("hot_small").with_(miss_rate=request.param)
+    print(f"[hot] workload={w.name} miss_rate={w.miss_rate}", flush=True)
     inp = synth.make_inputs(w, "cuda")
     arr = arrays(inp)
     ref = oracle_step(w, arr)
@@ -42,7 +43,7 @@ def test_hot_buffer_misses_counted(hot_case):
         s = ref["sel"][b, 0]
         s = s[s >= 0]
         missing = int((slot[b, s] < 0).sum())
-        assert missing == hot_miss["n_miss"][b] == int(np.floor(0.2 * s.size + 0.5))
+        assert missing == hot_miss["n_miss"][b] == int(np.floor(w.miss_rate * s.size + 0.5))
     assert np.all(hot_all["n_miss"] == 0)
 
 
