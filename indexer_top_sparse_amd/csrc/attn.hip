@@ -586,24 +586,27 @@ __global__ __launch_bounds__(64 * NW) void attn_bf16_kernel(AttnPlan p) {
 
 // ============================================================ latent (MLA)
 // Latent rows (d_qk 576, values = the first 512 dims of the same row), one
-// KV head, 64 query heads per workgroup in four 16-head blocks.  Two waves
-// share a head block: each computes half of the QK contraction (288 dims)
-// and owns half of the 512 output columns.
-//   S^T[32 tokens x 16 heads] = K_tile Q^T  (A = K rows from LDS, B = q in
-//       registers); the two partial S^T of a block are summed after one
-//       exchange through LDS, so both waves hold identical scores
-//   online softmax per head in registers, in the base-2 domain (scores are
-//       scaled by sm_scale * log2(e)); lane l holds head l % 16 and the four
-//       lanes of a head combine with permlane swaps
-//   O^T[256 x 16] += V^T P^T  (A = V^T read from the row-major tile with the
-//       LDS transpose load ds_read_b64_tr_b16, B = the lane's own
-//       probabilities)
+// KV head, 64 query heads per workgroup in four 16-head blocks.  The eight
+// waves split by role, so that on every SIMD a score wave and a P V wave
+// overlap instead of running the two phases back to back:
+//   score waves 0..3, head block w:
+//     S^T[32 tokens x 16 heads] = K_tile Q^T over all 576 dims (A = K rows
+//       from LDS, B = q in registers)
+//     online softmax per head in the base-2 domain (scores scaled by
+//       sm_scale * log2(e)); lane l holds head l % 16 and the four lanes of
+//       a head combine with permlane swaps; the bf16 probabilities and the
+//       factor that rescales each head's O go to LDS
+//   P V waves 4..7, columns [128 c, +128) of all 64 heads:
+//     O^T[128 x 16] += V^T P^T per head block (A = V^T read from the
+//       row-major tile with the LDS transpose load ds_read_b64_tr_b16, shared
+//       by the four head blocks; B = the block's probabilities)
 // The token order of the P V contraction is permuted so that the eight
-// probabilities a lane already holds (tokens 4g..4g+3 and 16+4g..16+4g+3,
-// g = lane / 16) are exactly its B operand.  K tiles rotate through three
-// LDS buffers with one more tile in flight in registers.  Probabilities
-// are taken relative to a per-head reference max that moves (rescaling O and
-// the sum) only when a tile's max exceeds it by more than 2^8.
+// probabilities a score lane holds (tokens 4g..4g+3 and 16+4g..16+4g+3,
+// g = lane / 16) are exactly one lane's B operand.  K tiles rotate through
+// three LDS buffers with one more tile in flight in registers; the score
+// waves run one tile ahead of the P V waves.  Probabilities are taken
+// relative to a per-head reference max that moves (rescaling O and the
+// sum) only when a tile's max exceeds it by more than 2^8.
 constexpr int kMlaWaves = 8;
 constexpr int kMlaHeadsWG = 64;
 constexpr int kMlaThreads = 64 * kMlaWaves;
@@ -639,7 +642,10 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const uint16_t* p) {
 
 __global__ __launch_bounds__(kMlaThreads, 1) void attn_mla_kernel(AttnPlan p) {
   __shared__ __attribute__((aligned(16))) uint16_t ks_s[3][kTT * kMlaRow];
-  __shared__ __attribute__((aligned(16))) f32x4 sx_s[2][kMlaWaves][2][64];  // partial S^T
+  // probabilities of a tile as the P V waves' B operands, [buffer][head block][lane]
+  __shared__ __attribute__((aligned(16))) bf16x8 pb_s[2][4][64];
+  __shared__ float alpha_s[2][4][16];  // rescale factor of each head's O for that tile
+  __shared__ float ml_s[kMlaHeadsWG][2];
   __shared__ uint64_t rowp_s[kMaxSplitTok + kMlaPad];
   __shared__ uint32_t vmask_s[kMaxSplitTok / kTT];  // valid tokens of each tile
 
@@ -653,11 +659,10 @@ __global__ __launch_bounds__(kMlaThreads, 1) void attn_mla_kernel(AttnPlan p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wid = tid >> 6;
-  const int hb = wid & 3;           // 16-head block
-  const int half = wid >> 2;        // QK dims [288 half, +288), columns [256 half, +256)
   const int g = lane >> 4;
   const int n = lane & 15;
-  const int head = grp * kMlaHeadsWG + hb * 16 + n;
+  const bool qk_wave = wid < 4;  // waves 0..3: scores and softmax of head block wid
+  const int cq = wid & 3;        // waves 4..7: P V for columns [128 cq, +128)
   const int32_t* selrow = p.sel + (int64_t)b * p.sel_heads * p.k;
   const int valid = valid_tokens(A, b);
   const int tps = (p.k_tokens + p.splits - 1) / p.splits;
@@ -667,16 +672,6 @@ __global__ __launch_bounds__(kMlaThreads, 1) void attn_mla_kernel(AttnPlan p) {
   const int ntiles = (cnt + kTT - 1) / kTT;
   const int64_t stage_base = (int64_t)b * p.sel_heads * p.k_tokens;
   RowAddr ra{A};
-
-  // q as the B operand: B[k = dim 32(9 half + s) + 8g + e][n = head]; its
-  // loads are issued first and complete while the row table is resolved
-  bf16x8 qb[9];
-  {
-    const uint16_t* qp = (const uint16_t*)A.q + (int64_t)b * A.q_stride_b +
-                         (int64_t)head * A.q_stride_h + 288 * half + 8 * g;
-#pragma unroll
-    for (int s = 0; s < 9; ++s) qb[s] = *(const bf16x8*)(qp + 32 * s);
-  }
 
   // Row table: the K row address of every split position (masked positions
   // and the prefetch pad point at a finite dummy row, so every load in the
@@ -700,17 +695,16 @@ __global__ __launch_bounds__(kMlaThreads, 1) void attn_mla_kernel(AttnPlan p) {
   for (int i = cnt + tid; i < (ntiles + 3) * kTT; i += kMlaThreads) rowp_s[i] = dummy;
 
   // gather coordinates: chunk i of this thread is row crow[i], byte offset
-  // coff[i] of the row, LDS element offset lofs[i] (-1: no chunk)
-  int crow[kMlaNch], coff[kMlaNch], lofs[kMlaNch];
+  // coff[i] of the row; the last chunk index may fall past the tile
+  int crow[kMlaNch], coff[kMlaNch];
 #pragma unroll
   for (int i = 0; i < kMlaNch; ++i) {
     const int q = tid + i * kMlaThreads;
     const int qc = q < kMlaChunks ? q : kMlaChunks - 1;
     crow[i] = qc / 72;
     coff[i] = 16 * (qc % 72);
-    lofs[i] = q < kMlaChunks ? crow[i] * kMlaRow + 8 * (qc % 72) : -1;
   }
-  __syncthreads();  // row table ready
+  const bool last_chunk = tid + (kMlaNch - 1) * kMlaThreads < kMlaChunks;
 
   auto gather = [&](u32x4 (&pre)[kMlaNch], int tile) __attribute__((always_inline)) {
 #pragma unroll
@@ -720,144 +714,192 @@ __global__ __launch_bounds__(kMlaThreads, 1) void attn_mla_kernel(AttnPlan p) {
   auto commit = [&](const u32x4 (&pre)[kMlaNch], int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < kMlaNch; ++i)
-      if (lofs[i] >= 0) *(u32x4*)(&ks_s[buf][lofs[i]]) = pre[i];
+      if (i < kMlaNch - 1 || last_chunk)
+        *(u32x4*)(&ks_s[buf][crow[i] * kMlaRow + (coff[i] >> 1)]) = pre[i];
   };
-
-  const float qk_scale = A.sm_scale * kLog2e;
-  float m_run = -__builtin_huge_valf();  // base-2 reference max
-  float l_run = 0.f;
-  // O^T accumulators: m-tile mt holds columns 256 half + 16 mt + 4g + i
-  f32x4 o[16];
-#pragma unroll
-  for (int mt = 0; mt < 16; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // phase 1 of a tile: this wave's partial S^T into LDS
-  auto qk_partial = [&](int buf, int sb) __attribute__((always_inline)) {
-    const uint16_t* kt = ks_s[buf];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
-      const uint16_t* kr = kt + (16 * mt + n) * kMlaRow + 288 * half + 8 * g;
-#pragma unroll
-      for (int s = 0; s < 9; ++s) {
-        bf16x8 kv = *(const bf16x8*)(kr + 32 * s);
-        if (s & 1) a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qb[s], a1, 0, 0, 0);
-        else a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qb[s], a0, 0, 0, 0);
-      }
-      sx_s[sb][wid][mt][lane] = a0 + a1;
-      __builtin_amdgcn_sched_barrier(0);  // bound the live K fragments
-    }
-  };
-
-  // phase 2: full scores, softmax, P V
-  const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3F803F80u);
-  auto finish = [&](int tile, int buf, int sb) __attribute__((always_inline)) {
-    const uint16_t* kt = ks_s[buf];
-    const uint32_t vm = __builtin_amdgcn_readfirstlane(vmask_s[tile]);
-    float sv[8];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      const f32x4 mine = sx_s[sb][wid][mt][lane];
-      const f32x4 other = sx_s[sb][wid ^ 4][mt][lane];
-      // identical in both waves of the block: IEEE addition commutes
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sv[4 * mt + i] = (mine[i] + other[i]) * qk_scale;
-    }
-    if (vm != 0xFFFFFFFFu) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (!((vm >> (16 * (e >> 2) + 4 * g + (e & 3))) & 1u)) sv[e] = -__builtin_huge_valf();
-    }
-    float tmax = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
-                       fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-    tmax = fmaxf(tmax, xlane16(tmax));
-    tmax = fmaxf(tmax, swap_halves(tmax));
-    constexpr float kSlack = 8.0f;
-    if (__builtin_amdgcn_ballot_w64(tmax > m_run + kSlack)) {
-      const float m_new = fmaxf(m_run, tmax);
-      const float alpha =
-          (m_run == -__builtin_huge_valf()) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-#pragma unroll
-      for (int mt = 0; mt < 16; ++mt) o[mt] *= alpha;
-      l_run *= alpha;
-      m_run = m_new;
-    }
-    const bool none = (m_run == -__builtin_huge_valf());
-    float psum = 0.f;
-    uint32_t pk[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float p0 = none ? 0.f : __builtin_amdgcn_exp2f(sv[2 * e] - m_run);
-      const float p1 = none ? 0.f : __builtin_amdgcn_exp2f(sv[2 * e + 1] - m_run);
-      const bf16x2 pp = bf16x2{(__bf16)p0, (__bf16)p1};
-      psum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, psum, false);
-      pk[e] = __builtin_bit_cast(uint32_t, pp);
-    }
-    psum += xlane16(psum);
-    psum += swap_halves(psum);
-    l_run += psum;
-    // B operand of P V: k = 8g + e  <->  token (e < 4 ? 4g + e : 16 + 4g + e - 4)
-    const bf16x8 pb = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
-    // A operand, m-tile mt: lane (g, n) needs column 256 half + 16 mt + n of
-    // those eight tokens; lane n of each group addresses token row n / 4 of
-    // the four and columns 4 (n % 4) .. +3
-    const uint16_t* vb = kt + (4 * g + (n >> 2)) * kMlaRow + 256 * half + 4 * (n & 3);
-#pragma unroll
-    for (int mt = 0; mt < 16; ++mt) {
-      const s16x4 r0 = lds_read_tr16(vb + 16 * mt);
-      const s16x4 r1 = lds_read_tr16(vb + 16 * kMlaRow + 16 * mt);
-      const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7));
-      o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, o[mt], 0, 0, 0);
-      if ((mt & 7) == 7) __builtin_amdgcn_sched_barrier(0);  // bound the live V fragments
-    }
-  };
-
-  // ---- pipeline, one barrier per tile.  In step t the workgroup finishes
-  // tile t (softmax, P V from LDS buffer t % 3 and partial scores t % 2),
-  // computes the partial scores of tile t+1 (buffer (t+1) % 3), writes tile
-  // t+2 from registers into buffer (t+2) % 3 and starts loading tile t+3.
-  // Tiles past the split are fully masked and only ever partially scored.
+  // the first three tiles: two in LDS, one in registers
   u32x4 pre[kMlaNch];
-  if (ntiles > 0) {
-    {
+  auto prologue = [&]() __attribute__((always_inline)) {
+    __syncthreads();  // row table ready
+    if (ntiles > 0) {
       u32x4 pre1[kMlaNch];
       gather(pre, 0);
       gather(pre1, 1);
       commit(pre, 0);
       commit(pre1, 1);
+      gather(pre, 2);
     }
-    gather(pre, 2);
     __syncthreads();
-    qk_partial(0, 0);
-    __syncthreads();
-    for (int t = 0; t < ntiles; ++t) {
-      commit(pre, (t + 2) % 3);
-      gather(pre, t + 3);
-      qk_partial((t + 1) % 3, (t + 1) & 1);
-      finish(t, t % 3, t & 1);
-      __syncthreads();
-    }
-  }
+  };
 
-  // ---- epilogue: lane holds O^T[col][head n], col = 256 half + 16 mt + 4g + i
-  const int64_t oh = (int64_t)b * A.n_q_heads + head;
-  if (p.splits == 1) {
-    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-    float* op = p.out + oh * 512 + 256 * half + 4 * g;
+  // ---- pipeline, one barrier per tile.  In step t the score waves compute
+  // the scores and probabilities of tile t+1 (LDS buffer (t+1) % 3) into
+  // probability buffer (t+1) % 2 while the P V waves consume tile t (buffer
+  // t % 3, probabilities t % 2); every thread writes tile t+2 from
+  // registers into buffer (t+2) % 3 and starts loading tile t+3.
+  if (qk_wave) {
+    // q of head block wid as the B operand: B[k = dim 32 s + 8g + e][n = head]
+    const int head = grp * kMlaHeadsWG + 16 * wid + n;
+    bf16x8 qb[18];
+    {
+      const uint16_t* qp = (const uint16_t*)A.q + (int64_t)b * A.q_stride_b +
+                           (int64_t)head * A.q_stride_h + 8 * g;
 #pragma unroll
-    for (int mt = 0; mt < 16; ++mt) *(f32x4*)(op + 16 * mt) = o[mt] * inv;
-    if (half == 0 && g == 0 && p.lse)
-      p.lse[oh] = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : -__builtin_huge_valf();
+      for (int s = 0; s < 18; ++s) qb[s] = *(const bf16x8*)(qp + 32 * s);
+    }
+    const float qk_scale = A.sm_scale * kLog2e;
+    float m_run = -__builtin_huge_valf();  // base-2 reference max
+    float l_run = 0.f;
+    const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3F803F80u);
+    // S^T[32 tokens x 16 heads] of one tile, online softmax, probabilities
+    // into LDS
+    auto scores = [&](int tile, int buf, int sb) __attribute__((always_inline)) {
+      const uint16_t* kt = ks_s[buf];
+      float sv[8];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+        const uint16_t* kr = kt + (16 * mt + n) * kMlaRow + 8 * g;
+#pragma unroll
+        for (int s = 0; s < 18; ++s) {
+          const bf16x8 kv = *(const bf16x8*)(kr + 32 * s);
+          if (s & 1) a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qb[s], a1, 0, 0, 0);
+          else a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qb[s], a0, 0, 0, 0);
+          if ((s % 6) == 5) __builtin_amdgcn_sched_barrier(0);  // bound the live K fragments
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sv[4 * mt + i] = (a0[i] + a1[i]) * qk_scale;
+      }
+      const uint32_t vm = __builtin_amdgcn_readfirstlane(vmask_s[tile]);
+      if (vm != 0xFFFFFFFFu) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (!((vm >> (16 * (e >> 2) + 4 * g + (e & 3))) & 1u)) sv[e] = -__builtin_huge_valf();
+      }
+      float tmax = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                         fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+      tmax = fmaxf(tmax, xlane16(tmax));
+      tmax = fmaxf(tmax, swap_halves(tmax));
+      constexpr float kSlack = 8.0f;
+      float alpha = 1.f;
+      if (__builtin_amdgcn_ballot_w64(tmax > m_run + kSlack)) {
+        const float m_new = fmaxf(m_run, tmax);
+        alpha = (m_run == -__builtin_huge_valf()) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= alpha;
+        m_run = m_new;
+      }
+      if (g == 0) alpha_s[sb][wid][n] = alpha;
+      const bool none = (m_run == -__builtin_huge_valf());
+      float psum = 0.f;
+      uint32_t pk[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p0 = none ? 0.f : __builtin_amdgcn_exp2f(sv[2 * e] - m_run);
+        const float p1 = none ? 0.f : __builtin_amdgcn_exp2f(sv[2 * e + 1] - m_run);
+        const bf16x2 pp = bf16x2{(__bf16)p0, (__bf16)p1};
+        psum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, psum, false);
+        pk[e] = __builtin_bit_cast(uint32_t, pp);
+      }
+      psum += xlane16(psum);
+      psum += swap_halves(psum);
+      l_run += psum;
+      // B operand of P V: k = 8g + e  <->  token (e < 4 ? 4g + e : 16 + 4g + e - 4)
+      pb_s[sb][wid][lane] = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+    };
+    prologue();
+    if (ntiles > 0) {
+      scores(0, 0, 0);
+      __syncthreads();
+      for (int t = 0; t < ntiles; ++t) {
+        commit(pre, (t + 2) % 3);
+        gather(pre, t + 3);
+        if (t + 1 < ntiles) scores(t + 1, (t + 1) % 3, (t + 1) & 1);
+        __syncthreads();
+      }
+    }
+    if (g == 0) {
+      ml_s[16 * wid + n][0] = m_run;
+      ml_s[16 * wid + n][1] = l_run;
+    }
+    __syncthreads();
+    const int64_t oh = (int64_t)b * A.n_q_heads + head;
+    if (p.splits == 1) {
+      if (g == 0 && p.lse)
+        p.lse[oh] = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : -__builtin_huge_valf();
+    } else if (g == 0) {
+      float* pr = p.part + (((int64_t)b * ngrp + grp) * p.splits + split) * kMlaRec;
+      pr[kMlaHeadsWG * 512 + 2 * (16 * wid + n)] = m_run;
+      pr[kMlaHeadsWG * 512 + 2 * (16 * wid + n) + 1] = l_run;
+    }
   } else {
-    // record of (request, head group, split) in register order: slot
-    // wave * 16 + mt holds one f32x4 per lane, so that every store writes
-    // 1 KiB contiguously; then (m, l) per head
-    float* pp = p.part + (((int64_t)b * ngrp + grp) * p.splits + split) * kMlaRec;
+    // O^T accumulators: o[hb][mc] holds columns 128 cq + 16 mc + 4g + i of
+    // head 16 hb + n of the group
+    f32x4 o[4][8];
 #pragma unroll
-    for (int mt = 0; mt < 16; ++mt) *(f32x4*)(pp + ((wid * 16 + mt) * 64 + lane) * 4) = o[mt];
-    if (half == 0 && g == 0) {
-      pp[kMlaHeadsWG * 512 + 2 * (hb * 16 + n)] = m_run;
-      pp[kMlaHeadsWG * 512 + 2 * (hb * 16 + n) + 1] = l_run;
+    for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+      for (int mc = 0; mc < 8; ++mc) o[hb][mc] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // O^T[128 x 64] += V^T P^T for one tile; each V fragment feeds the four
+    // head blocks
+    auto pv = [&](int buf, int sb) __attribute__((always_inline)) {
+      const uint16_t* kt = ks_s[buf];
+      bf16x8 pbk[4];
+#pragma unroll
+      for (int hb = 0; hb < 4; ++hb) {
+        const float alpha = alpha_s[sb][hb][n];
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+#pragma unroll
+          for (int mc = 0; mc < 8; ++mc) o[hb][mc] *= alpha;
+        }
+        pbk[hb] = pb_s[sb][hb][lane];
+      }
+      // A operand, m-tile mc: lane (g, n) needs column 128 cq + 16 mc + n of
+      // the eight tokens of its k range; lane n of each group addresses
+      // token row n / 4 of the four and columns 4 (n % 4) .. +3
+      const uint16_t* vb = kt + (4 * g + (n >> 2)) * kMlaRow + 128 * cq + 4 * (n & 3);
+#pragma unroll
+      for (int mc = 0; mc < 8; ++mc) {
+        const s16x4 r0 = lds_read_tr16(vb + 16 * mc);
+        const s16x4 r1 = lds_read_tr16(vb + 16 * kMlaRow + 16 * mc);
+        const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb)
+          o[hb][mc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pbk[hb], o[hb][mc], 0, 0, 0);
+        if ((mc & 3) == 3) __builtin_amdgcn_sched_barrier(0);  // bound the live V fragments
+      }
+    };
+    prologue();
+    if (ntiles > 0) {
+      __syncthreads();
+      for (int t = 0; t < ntiles; ++t) {
+        commit(pre, (t + 2) % 3);
+        gather(pre, t + 3);
+        pv(t % 3, t & 1);
+        __syncthreads();
+      }
+    }
+    __syncthreads();  // (m, l) of every head in LDS
+    // epilogue: o[hb][mc] = O^T[col 128 cq + 16 mc + 4g + i][head 16 hb + n]
+    if (p.splits == 1) {
+#pragma unroll
+      for (int hb = 0; hb < 4; ++hb) {
+        const float l = ml_s[16 * hb + n][1];
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        const int64_t oh = (int64_t)b * A.n_q_heads + grp * kMlaHeadsWG + 16 * hb + n;
+        float* op = p.out + oh * 512 + 128 * cq + 4 * g;
+#pragma unroll
+        for (int mc = 0; mc < 8; ++mc) *(f32x4*)(op + 16 * mc) = o[hb][mc] * inv;
+      }
+    } else {
+      // record of (request, head group, split) in register order: slot
+      // (cq * 4 + hb) * 8 + mc holds one f32x4 per lane, so that every store
+      // writes 1 KiB contiguously; (m, l) per head follow
+      float* pr = p.part + (((int64_t)b * ngrp + grp) * p.splits + split) * kMlaRec;
+#pragma unroll
+      for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+        for (int mc = 0; mc < 8; ++mc)
+          *(f32x4*)(pr + ((((cq * 4 + hb) * 8) + mc) * 64 + lane) * 4) = o[hb][mc];
     }
   }
 }
@@ -942,48 +984,52 @@ __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(AttnPlan p) 
 }
 
 // Latent records (register order of the attention kernel, base-2 m): one
-// workgroup per (request, head group, attention wave); thread (q, lane)
-// merges slots 2q and 2q + 1 of that wave's lane.
+// workgroup per (request, head group, column quarter cq); thread (q, lane)
+// merges slots 4q .. 4q + 3 of quarter cq: head block q / 2, column m-tiles
+// 4 (q % 2) .. +3.
 __global__ __launch_bounds__(512) void attn_combine_mla_kernel(AttnPlan p) {
   const sparse_attn_args& A = p.a;
   const int ngrp = A.n_q_heads / kMlaHeadsWG;
-  const int wv = (int)(blockIdx.x % kMlaWaves);
-  const int64_t bg = blockIdx.x / kMlaWaves;  // request * ngrp + group
+  const int cq = (int)(blockIdx.x % 4);
+  const int64_t bg = blockIdx.x / 4;  // request * ngrp + group
   const int b = (int)(bg / ngrp), grp = (int)(bg % ngrp);
   const int tid = threadIdx.x, lane = tid & 63, q = tid >> 6;
-  const int hb = wv & 3, half = wv >> 2, g = lane >> 4, n = lane & 15;
-  const int hl = hb * 16 + n;
+  const int g = lane >> 4, n = lane & 15;
+  const int hb = q >> 1, mc0 = 4 * (q & 1);
+  const int hl = 16 * hb + n;
   const int S = p.splits;
   const float* base = p.part + bg * S * kMlaRec;
   float M = -__builtin_huge_valf();
   for (int sp = 0; sp < S; ++sp)
     M = fmaxf(M, base[(int64_t)sp * kMlaRec + kMlaHeadsWG * 512 + 2 * hl]);
   float L = 0.f;
-  f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
-  const int slot = wv * 16 + 2 * q;
+  f32x4 acc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int slot = (cq * 4 + hb) * 8 + mc0;
   for (int sp = 0; sp < S; ++sp) {
     const float* ps = base + (int64_t)sp * kMlaRec;
     const float l = ps[kMlaHeadsWG * 512 + 2 * hl + 1];
     if (l > 0.f) {
       const float f = __builtin_amdgcn_exp2f(ps[kMlaHeadsWG * 512 + 2 * hl] - M);
       L += l * f;
-      a0 += *(const f32x4*)(ps + (slot * 64 + lane) * 4) * f;
-      a1 += *(const f32x4*)(ps + ((slot + 1) * 64 + lane) * 4) * f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[j] += *(const f32x4*)(ps + ((slot + j) * 64 + lane) * 4) * f;
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
   const int64_t oh = (int64_t)b * A.n_q_heads + grp * kMlaHeadsWG + hl;
-  float* op = p.out + oh * 512 + 256 * half + 32 * q + 4 * g;
-  *(f32x4*)op = a0 * inv;
-  *(f32x4*)(op + 16) = a1 * inv;
-  if (q == 0 && half == 0 && g == 0 && p.lse)
+  float* op = p.out + oh * 512 + 128 * cq + 16 * mc0 + 4 * g;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) *(f32x4*)(op + 16 * j) = acc[j] * inv;
+  if ((q & 1) == 0 && cq == 0 && g == 0 && p.lse)
     p.lse[oh] = L > 0.f ? (M + __log2f(L)) * kLn2 : -__builtin_huge_valf();
 }
 
 hipError_t launch_attn_combine(const AttnPlan& p, hipStream_t s) {
   const sparse_attn_args& a = p.a;
   if (a.dtype == SPARSE_BF16 && mla_shape(a)) {
-    const int64_t wgs = (int64_t)a.batch * (a.n_q_heads / kMlaHeadsWG) * kMlaWaves;
+    const int64_t wgs = (int64_t)a.batch * (a.n_q_heads / kMlaHeadsWG) * 4;
     attn_combine_mla_kernel<<<(unsigned)wgs, 512, 0, s>>>(p);
   } else {
     attn_combine_kernel<<<(unsigned)((int64_t)a.batch * a.n_q_heads), kCombThreads, 0, s>>>(p);
