@@ -98,7 +98,7 @@ int attn_splits(const sparse_attn_args& a, int k_tokens) {
     min_tok = 16;
     target = 256;
   } else if (a.d_qk == 576) {
-    // one 4-wave workgroup per compute unit, 64 heads each
+    // one 8-wave workgroup per compute unit, 64 heads each
     groups = a.n_q_heads / 64;
     min_tok = 256;
     target = 256;

@@ -999,23 +999,40 @@ __global__ __launch_bounds__(512) void attn_combine_mla_kernel(AttnPlan p) {
   const int hl = 16 * hb + n;
   const int S = p.splits;
   const float* base = p.part + bg * S * kMlaRec;
-  float M = -__builtin_huge_valf();
-  for (int sp = 0; sp < S; ++sp)
-    M = fmaxf(M, base[(int64_t)sp * kMlaRec + kMlaHeadsWG * 512 + 2 * hl]);
-  float L = 0.f;
+  const int slot = (cq * 4 + hb) * 8 + mc0;
+  // splits in batches of four, every load of a batch issued before any is
+  // used; the batches merge online (running max M, sum L, output acc)
+  float M = -__builtin_huge_valf(), L = 0.f;
   f32x4 acc[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int slot = (cq * 4 + hb) * 8 + mc0;
-  for (int sp = 0; sp < S; ++sp) {
-    const float* ps = base + (int64_t)sp * kMlaRec;
-    const float l = ps[kMlaHeadsWG * 512 + 2 * hl + 1];
-    if (l > 0.f) {
-      const float f = __builtin_amdgcn_exp2f(ps[kMlaHeadsWG * 512 + 2 * hl] - M);
-      L += l * f;
+  for (int s0 = 0; s0 < S; s0 += 4) {
+    float mv[4], lv[4];
+    f32x4 pv[4][4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[j] += *(const f32x4*)(ps + ((slot + j) * 64 + lane) * 4) * f;
+    for (int u = 0; u < 4; ++u) {
+      const float* ps = base + (int64_t)min(s0 + u, S - 1) * kMlaRec;
+      mv[u] = ps[kMlaHeadsWG * 512 + 2 * hl];
+      lv[u] = s0 + u < S ? ps[kMlaHeadsWG * 512 + 2 * hl + 1] : 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) pv[u][j] = *(const f32x4*)(ps + ((slot + j) * 64 + lane) * 4);
     }
+    float mb = M;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (lv[u] > 0.f) mb = fmaxf(mb, mv[u]);
+    const float r = M == -__builtin_huge_valf() ? 0.f : __builtin_amdgcn_exp2f(M - mb);
+    L *= r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] *= r;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float f = lv[u] > 0.f ? __builtin_amdgcn_exp2f(mv[u] - mb) : 0.f;
+      L += lv[u] * f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[j] += pv[u][j] * f;
+    }
+    M = mb;
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
   const int64_t oh = (int64_t)b * A.n_q_heads + grp * kMlaHeadsWG + hl;
