@@ -49,7 +49,7 @@ struct IndexLayout {
   int n_chunks = 0;
   int hist_parts = 0;   // histogram parts per row the score kernel writes
   size_t scores = 0, hist = 0, bstar = 0, cand_key = 0, cand_idx = 0, chunk_cnt = 0,
-         depth = 0, plist = 0, pwl = 0, npl = 0, score_c = 0, end = 0;
+         cand_total = 0, depth = 0, plist = 0, pwl = 0, npl = 0, score_c = 0, end = 0;
 };
 
 IndexLayout index_layout(const sparse_index_args& a, bool with_scores) {
@@ -67,11 +67,12 @@ IndexLayout index_layout(const sparse_index_args& a, bool with_scores) {
   // standalone top-k)
   L.hist_parts = sd::score_hist_parts(a);
   const int parts = std::max(L.hist_parts, std::max(L.n_chunks, 1));
-  L.hist = take((size_t)L.rows * parts * sd::kHistWords * 4);
+  L.hist = take((size_t)L.rows * parts * sd::kHistPartWords * 4);
   L.bstar = take((size_t)L.rows * 2 * 4);
   L.cand_key = take(cells * 4);
   L.cand_idx = take(cells * 4);
   L.chunk_cnt = take((size_t)L.rows * std::max(L.n_chunks, 1) * 4);
+  L.cand_total = take((size_t)L.rows * 4);
   if (a.kind == SPARSE_SCORE_BITPLANE) {
     const size_t hd = (size_t)a.batch * a.n_kv_heads * a.head_dim;
     L.depth = take(hd);
@@ -235,7 +236,7 @@ int check_attn(const sparse_attn_args* a, int sel_heads, int k, int sel_unit) {
 sd::TopkPlan make_topk_plan(const IndexLayout& L, char* ws, const float* scores,
                             int64_t row_stride, const int32_t* valid, int rows_per_valid,
                             int unit_div, int k, int32_t* idx_out, float* val_out,
-                            int hist_parts) {
+                            int hist_parts, int part_span) {
   sd::TopkPlan p;
   p.rows = L.rows;
   p.n_units = L.n_units;
@@ -248,7 +249,13 @@ sd::TopkPlan make_topk_plan(const IndexLayout& L, char* ws, const float* scores,
   p.unit_div = unit_div;
   p.hist = (uint32_t*)(ws + L.hist);
   p.parts = hist_parts;
+  p.part_span = part_span;
+  // one contiguous candidate list per row when the parts are few contiguous
+  // spans that cover the row
+  p.fused = part_span > 0 && hist_parts >= 1 && hist_parts <= sd::kFuseMaxParts &&
+            (int64_t)hist_parts * part_span >= L.n_units;
   p.bstar = (uint32_t*)(ws + L.bstar);
+  p.cand_total = (uint32_t*)(ws + L.cand_total);
   p.cand_key = (uint32_t*)(ws + L.cand_key);
   p.cand_idx = (int32_t*)(ws + L.cand_idx);
   p.chunk_cnt = (uint32_t*)(ws + L.chunk_cnt);
@@ -265,8 +272,12 @@ int run_topk(const sd::TopkPlan& p, bool hist_ready, hipStream_t s) {
     return SPARSE_OK;
   }
   if (!hist_ready) HIPCHECK(sd::launch_topk_hist(p, s));
-  HIPCHECK(sd::launch_topk_bin(p, s));
-  HIPCHECK(sd::launch_topk_filter(p, s));
+  if (p.fused) {
+    HIPCHECK(sd::launch_topk_filter_fused(p, s));
+  } else {
+    HIPCHECK(sd::launch_topk_bin(p, s));
+    HIPCHECK(sd::launch_topk_filter(p, s));
+  }
   HIPCHECK(sd::launch_topk_select(p, s));
   return SPARSE_OK;
 }
@@ -427,7 +438,7 @@ int sparse_topk(const float* scores, int32_t rows, int32_t n_units, int64_t row_
   IndexLayout L = index_layout(a, false);
   sd::TopkPlan p = make_topk_plan(L, (char*)ws, scores, row_stride, valid_units,
                                   valid_units ? rows_per_valid : 1, 1, k, idx_out, val_out,
-                                  L.n_chunks);
+                                  L.n_chunks, sd::kTopkChunk);
   return run_topk(p, false, (hipStream_t)stream);
 }
 
@@ -471,7 +482,8 @@ int sparse_decode_step(const sparse_index_args* ia, const sparse_attn_args* aa, 
   IndexLayout L = index_layout(*ia, true);
   float* scores = (float*)(w + L.scores);
   sd::TopkPlan tp = make_topk_plan(L, w, scores, L.n_units, ia->seq_lens, L.rows_per_b,
-                                   unit, k, topk_out, nullptr, L.hist_parts);
+                                   unit, k, topk_out, nullptr, L.hist_parts,
+                                   sd::score_part_span(*ia));
   if (ia->n > 0) {
     rc = run_scores(*ia, L, w, scores, tp.hist, s);
     if (rc) return rc;

@@ -27,6 +27,14 @@ constexpr int kHistBins = 4096;
 // kHistPartMax units.
 constexpr int kHistWords = kHistBins / 2;
 constexpr int kHistPartMax = 65535;
+// Each part is followed by kCoarseBins 32-bit coarse counts (sums of 64
+// consecutive bins), so that a consumer finds the boundary bin from the
+// coarse counts and the 64 bins of one coarse bin instead of all 4096.
+constexpr int kCoarseBins = 64;
+constexpr int kHistPartWords = kHistWords + kCoarseBins;
+// Rows whose parts are at most this many contiguous unit spans take the
+// fused filter (no separate bin kernel).
+constexpr int kFuseMaxParts = 64;
 
 // Pointer into the global address space: loads through it compile to
 // global_load (vector memory counter only) rather than flat_load.
@@ -48,6 +56,21 @@ __device__ __forceinline__ uint32_t score_key(float x) {
 __device__ __forceinline__ float key_score(uint32_t k) {
   uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
   return __uint_as_float(u);
+}
+
+// Store an LDS histogram h[kHistBins] as one part: the 16-bit counts in
+// pairs, then the coarse counts.  Needs at least 256 threads (whole waves).
+__device__ __forceinline__ void store_hist_part(const uint32_t* h, uint32_t* part, int nt) {
+  for (int i = threadIdx.x; i < kHistWords; i += nt) part[i] = h[2 * i] | (h[2 * i + 1] << 16);
+  if (threadIdx.x < 4 * kCoarseBins) {
+    const int c = threadIdx.x >> 2, q = threadIdx.x & 3;
+    uint32_t s = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s += h[64 * c + 16 * q + i];
+    s += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)s, 0xB1, 0xF, 0xF, false);  // quad [1,0,3,2]
+    s += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)s, 0x4E, 0xF, 0xF, false);  // quad [2,3,0,1]
+    if (q == 0) part[kHistWords + c] = s;
+  }
 }
 
 // Cross-half exchange: value of lane l ^ 32.
@@ -79,6 +102,24 @@ __device__ __forceinline__ float row16_sum(float x) {
   return x;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave, entirely in DPP: shifts
+// by 1, 2, 4 and 8 within each row of 16 lanes (lanes shifted past the row
+// start add 0), then the row totals carried by the row broadcasts of lane 15
+// (into rows 1 and 3) and lane 31 (into rows 2 and 3).
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return x;
+}
+// Sum over the wave, in every lane.
+__device__ __forceinline__ int wave_sum(int x) {
+  return __builtin_amdgcn_readlane(wave_incl_scan(x), 63);
+}
+
 // ---------------------------------------------------------------- block scan
 // Inclusive prefix sum over a block of NT threads (NT multiple of 64).
 // `lds` must hold NT/64 + 1 ints.  Returns the inclusive sum for the thread
@@ -89,21 +130,11 @@ __device__ __forceinline__ int block_inclusive_scan(int v, int* lds,
   constexpr int NW = NT / kWave;
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    int y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
+  const int x = wave_incl_scan(v);
   if (lane == 63) lds[wid] = x;
   __syncthreads();
   if (wid == 0) {
-    int w = lane < NW ? lds[lane] : 0;
-#pragma unroll
-    for (int off = 1; off < NW; off <<= 1) {
-      int y = __shfl_up(w, off, 64);
-      if (lane >= off) w += y;
-    }
+    const int w = wave_incl_scan(lane < NW ? lds[lane] : 0);
     if (lane < NW) lds[lane] = w;
   }
   __syncthreads();
@@ -126,9 +157,12 @@ struct TopkPlan {
   const float* scores;
   const int32_t* valid;
   int32_t unit_div;  // valid units = ceil(valid / unit_div)
-  uint32_t* hist;    // [rows][parts][kHistWords] 16-bit counts in pairs
+  uint32_t* hist;    // [rows][parts][kHistPartWords]: 16-bit counts in pairs, coarse counts
   int parts;         // histogram parts per row
+  int part_span;     // units per part (part q: units [q span, (q + 1) span))
+  int fused;         // candidates in one contiguous list per row (fused filter)
   uint32_t* bstar;   // [rows][2]: boundary bin b*, units in higher bins
+  uint32_t* cand_total;  // [rows]: candidates of the row (fused filter)
   uint32_t* cand_key;  // [rows][n_units]
   int32_t* cand_idx;   // [rows][n_units]
   uint32_t* chunk_cnt; // [rows][n_chunks]
@@ -140,6 +174,7 @@ struct TopkPlan {
 hipError_t launch_topk_hist(const TopkPlan& p, hipStream_t s);
 hipError_t launch_topk_bin(const TopkPlan& p, hipStream_t s);
 hipError_t launch_topk_filter(const TopkPlan& p, hipStream_t s);
+hipError_t launch_topk_filter_fused(const TopkPlan& p, hipStream_t s);
 hipError_t launch_topk_select(const TopkPlan& p, hipStream_t s);
 
 struct ScorePlan {
@@ -153,8 +188,10 @@ struct ScorePlan {
   int32_t* npl;      //   [B][Hkv] number of read planes
   float* score_c;    // BITPLANE: [B][Hkv] constant term
 };
-// Histogram parts per row that the score kernel of `a` writes.
+// Histogram parts per row that the score kernel of `a` writes, and the
+// units each covers (0 when a part is not one contiguous span).
 int score_hist_parts(const sparse_index_args& a);
+int score_part_span(const sparse_index_args& a);
 hipError_t launch_score_dot(const ScorePlan& p, hipStream_t s);
 hipError_t launch_score_lightning(const ScorePlan& p, hipStream_t s);
 hipError_t launch_read_depth(const sparse_index_args* a, int8_t* depth, int32_t* plist,

@@ -28,10 +28,7 @@ struct LdsHist {
     __syncthreads();
   }
   __device__ void add(float s) { atomicAdd(&h[score_key(s) >> 20], 1u); }
-  __device__ void store(uint32_t* part, int nt) {
-    for (int i = threadIdx.x; i < kHistWords; i += nt)
-      part[i] = h[2 * i] | (h[2 * i + 1] << 16);
-  }
+  __device__ void store(uint32_t* part, int nt) { store_hist_part(h, part, nt); }
 };
 
 __device__ __forceinline__ int valid_len(const int32_t* seq_lens, int b,
@@ -241,7 +238,7 @@ __global__ __launch_bounds__(kDotThreads) void score_dot_kernel(
   }
   if (hist) {
     __syncthreads();
-    lh.store(hist + ((int64_t)b * gridDim.x + blockIdx.x) * kHistWords, kDotThreads);
+    lh.store(hist + ((int64_t)b * gridDim.x + blockIdx.x) * kHistPartWords, kDotThreads);
   }
 }
 
@@ -439,7 +436,7 @@ __global__ __launch_bounds__(kLtThreads) void score_lightning_kernel(
   }
   if (hist) {
     __syncthreads();
-    lh.store(hist + ((int64_t)b * gridDim.x + blockIdx.x) * kHistWords, kLtThreads);
+    lh.store(hist + ((int64_t)b * gridDim.x + blockIdx.x) * kHistPartWords, kLtThreads);
   }
 }
 
@@ -685,7 +682,7 @@ __global__ __launch_bounds__(kBpThreads) void score_bitplane_kernel(
   }
   if (hist) {
     __syncthreads();
-    lh.store(hist + (bh * gridDim.x + blockIdx.x) * kHistWords, kBpThreads);
+    lh.store(hist + (bh * gridDim.x + blockIdx.x) * kHistPartWords, kBpThreads);
   }
 }
 
@@ -695,6 +692,17 @@ hipError_t launch_score_bitplane(const ScorePlan& p, hipStream_t s) {
   score_bitplane_kernel<<<grid, kBpThreads, 0, s>>>(a, p.plist, p.pwl, p.npl, p.score_c,
                                                    p.scores, p.hist, p.n_units);
   return hipGetLastError();
+}
+
+int score_part_span(const sparse_index_args& a) {
+  switch (a.kind) {
+    case SPARSE_SCORE_DOT:
+      return dot_rounds(a) * kDotRound / (a.block_size == 1 ? 1 : kDotTile);
+    case SPARSE_SCORE_LIGHTNING:
+      return (lightning_long(a) ? kLtLong : kLtShort) * kLtStride;
+    default:
+      return 0;  // bit-plane parts take passes grid-stride
+  }
 }
 
 int score_hist_parts(const sparse_index_args& a) {
