@@ -1057,37 +1057,68 @@ hipError_t launch_attn_combine(const AttnPlan& p, hipStream_t s) {
 // ============================================================ miss fetch
 // "XM-Sparse" blog, Figure 1 caption and KV-lifecycle list: selected
 // entries that are not in the HBM hot buffer are fetched from host memory.
-// One thread per 16-byte chunk of a missed row: reads the row through the
-// device-visible alias of the pinned host buffer (PCIe) and writes it to the
-// workspace staging slot of its selection position.
-__global__ __launch_bounds__(256) void miss_fetch_kernel(AttnPlan p) {
+// One workgroup per 256 selection positions of a request: each thread checks
+// one position once (token, then hot slot), the missed rows are compacted
+// into an LDS list (wave ballots), and the workgroup then copies those rows
+// 16 bytes per thread and item, eight items in flight, through the
+// device-visible alias of the pinned host buffer (PCIe) into the workspace
+// staging slots of their selection positions.
+constexpr int kMfRows = 256;
+constexpr int kMfUnroll = 8;
+
+__global__ __launch_bounds__(kMfRows) void miss_fetch_kernel(AttnPlan p) {
+  __shared__ int32_t mj_s[kMfRows];
+  __shared__ const char* msrc_s[kMfRows];
+  __shared__ int nm_s;
   const sparse_attn_args& A = p.a;
   const int b = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int cpr = A.d_qk * 2 / 16;
-  const int valid = valid_tokens(A, b);
-  const int32_t* selrow = p.sel + (int64_t)b * p.sel_heads * p.k;
-  const int64_t total = (int64_t)p.k_tokens * cpr;
-  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < total;
-       q += (int64_t)gridDim.x * blockDim.x) {
-    const int j = (int)(q / cpr);
-    const int cc = (int)(q % cpr);
-    const int t = sel_token(selrow, j, p.sel_unit, valid);
-    if (t < 0) continue;
-    if (A.hot_slot[(int64_t)b * A.hs_stride_b + t] >= 0) continue;
-    const char* src = (const char*)A.host_kv +
-                      ((int64_t)b * A.host_stride_b + (int64_t)t * A.host_stride_t) * 2;
-    uint16_t* dst = p.staging + ((int64_t)b * p.k_tokens + j) * A.d_qk;
-    *(uint4*)((char*)dst + 16 * cc) = *(const uint4*)(src + 16 * cc);
+  if (tid == 0) nm_s = 0;
+  __syncthreads();
+  const int j = blockIdx.x * kMfRows + tid;
+  bool miss = false;
+  const char* src = nullptr;
+  if (j < p.k_tokens) {
+    const int32_t* selrow = p.sel + (int64_t)b * p.sel_heads * p.k;
+    const int t = sel_token(selrow, j, p.sel_unit, valid_tokens(A, b));
+    if (t >= 0 && A.hot_slot[(int64_t)b * A.hs_stride_b + t] < 0) {
+      miss = true;
+      src = (const char*)A.host_kv + ((int64_t)b * A.host_stride_b + (int64_t)t * A.host_stride_t) * 2;
+    }
+  }
+  const uint64_t bal = __builtin_amdgcn_ballot_w64(miss);
+  int base = 0;
+  if (lane == 0 && bal) base = atomicAdd(&nm_s, __builtin_popcountll(bal));
+  base = __shfl(base, 0, 64);
+  if (miss) {
+    const int slot = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                           __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+    mj_s[slot] = j;
+    msrc_s[slot] = src;
+  }
+  __syncthreads();
+  const int items = nm_s * cpr;
+  char* stage = (char*)(p.staging + (int64_t)b * p.k_tokens * A.d_qk);
+  for (int i0 = tid; i0 < items; i0 += kMfRows * kMfUnroll) {
+    uint4 v[kMfUnroll];
+#pragma unroll
+    for (int u = 0; u < kMfUnroll; ++u) {
+      const int i = i0 + u * kMfRows;
+      if (i < items) v[u] = *(const uint4*)(msrc_s[i / cpr] + 16 * (i % cpr));
+    }
+#pragma unroll
+    for (int u = 0; u < kMfUnroll; ++u) {
+      const int i = i0 + u * kMfRows;
+      if (i < items)
+        *(uint4*)(stage + (int64_t)mj_s[i / cpr] * A.d_qk * 2 + 16 * (i % cpr)) = v[u];
+    }
   }
 }
 
 hipError_t launch_miss_fetch(const AttnPlan& p, hipStream_t s) {
-  const int cpr = p.a.d_qk * 2 / 16;
-  int64_t per_b = (int64_t)p.k_tokens * cpr;
-  int gx = (int)((per_b + 255) / 256);
-  if (gx > 64) gx = 64;
-  dim3 grid(gx, p.a.batch);
-  miss_fetch_kernel<<<grid, 256, 0, s>>>(p);
+  dim3 grid((unsigned)((p.k_tokens + kMfRows - 1) / kMfRows), p.a.batch);
+  miss_fetch_kernel<<<grid, kMfRows, 0, s>>>(p);
   return hipGetLastError();
 }
 

@@ -449,9 +449,22 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkPlan p) {
   // level-2 histogram (bits [19:8] of the keys in bin b1), counted while
   // the candidates are staged
   for (int i = tid; i < kHistBins; i += kSelThreads) hs[i] = 0u;
-  // candidate count and (per-chunk slices) chunk offsets
+  // candidate count and (per-chunk slices) chunk offsets.  The fused
+  // filter's list starts at the row base, so its first kSelSpec * kSelThreads
+  // entries are loaded together with the count (one round trip).
+  constexpr int kSelSpec = 4;
+  uint32_t skey[kSelSpec];
+  int32_t sidx[kSelSpec];
   int M = 0;
   if (p.fused) {
+    const uint32_t* ck0 = p.cand_key + (int64_t)r * p.n_units;
+    const int32_t* ci0 = p.cand_idx + (int64_t)r * p.n_units;
+#pragma unroll
+    for (int j = 0; j < kSelSpec; ++j) {
+      const int q = tid + j * kSelThreads;
+      skey[j] = q < p.n_units ? ck0[q] : 0u;
+      sidx[j] = q < p.n_units ? ci0[q] : 0;
+    }
     M = min((int)p.cand_total[r], p.n_units);
     __syncthreads();
   } else {
@@ -479,7 +492,16 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkPlan p) {
   // chunks w, w + 16, ...
   const bool inlds = M <= kSelCap;
   if (inlds && p.fused) {
-    for (int q = tid; q < M; q += kSelThreads) {
+#pragma unroll
+    for (int j = 0; j < kSelSpec; ++j) {
+      const int q = tid + j * kSelThreads;
+      if (q < M) {
+        ckey_s[q] = skey[j];
+        cidx_s[q] = sidx[j];
+        if ((skey[j] >> 20) == b1) atomicAdd(&hs[(skey[j] >> 8) & 0xFFFu], 1u);
+      }
+    }
+    for (int q = tid + kSelSpec * kSelThreads; q < M; q += kSelThreads) {
       const uint32_t key = ck[q];
       ckey_s[q] = key;
       cidx_s[q] = ci[q];
