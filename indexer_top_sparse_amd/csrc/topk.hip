@@ -235,9 +235,8 @@ hipError_t launch_topk_filter(const TopkPlan& p, hipStream_t s) {
 // contiguous candidate list, so the candidates are written in index order
 // straight to their final place.  Part 0 stores b*, the units above it and
 // the row's candidate count for the select.
-constexpr int kFfThreads = 512;
-constexpr int kFfPer = 16;                    // units per thread and pass
-constexpr int kFfPass = kFfThreads * kFfPer;  // 8192
+// NT threads, PER units per thread and pass: 512 x 16 for long parts,
+// 256 x 16 or 256 x 8 for parts of at most 4096 or 2048 units.
 
 // (counts stay below 2^31)
 __device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t x, int) {
@@ -245,7 +244,9 @@ __device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t x, int) {
 }
 __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t x) { return (uint32_t)wave_sum((int)x); }
 
-__global__ __launch_bounds__(kFfThreads) void topk_filter_fused_kernel(TopkPlan p) {
+template <int NT, int PER>
+__global__ __launch_bounds__(NT) void topk_filter_fused_kernel(TopkPlan p) {
+  constexpr int kFfThreads = NT, kFfPer = PER, kFfPass = NT * PER;
   constexpr int NW = kFfThreads / kWave;
   constexpr int PPW = kFuseMaxParts / NW;  // parts per wave: q = wave + NW i
   __shared__ uint32_t ptot[NW][64];
@@ -404,7 +405,9 @@ __global__ __launch_bounds__(kFfThreads) void topk_filter_fused_kernel(TopkPlan 
 
 hipError_t launch_topk_filter_fused(const TopkPlan& p, hipStream_t s) {
   dim3 grid(p.parts, p.rows);
-  topk_filter_fused_kernel<<<grid, kFfThreads, 0, s>>>(p);
+  if (p.part_span > 4096) topk_filter_fused_kernel<512, 16><<<grid, 512, 0, s>>>(p);
+  else if (p.part_span > 2048) topk_filter_fused_kernel<256, 16><<<grid, 256, 0, s>>>(p);
+  else topk_filter_fused_kernel<256, 8><<<grid, 256, 0, s>>>(p);
   return hipGetLastError();
 }
 
