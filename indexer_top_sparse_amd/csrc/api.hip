@@ -104,9 +104,10 @@ int attn_splits(const sparse_attn_args& a, int k_tokens) {
     min_tok = 256;
     target = 256;
   } else {
+    // two 4-wave workgroups per compute unit, KV head each
     groups = a.n_kv_heads;
     min_tok = 64;
-    target = 1024;
+    target = 512;
   }
   const int64_t base = (int64_t)std::max(a.batch, 1) * std::max(groups, 1);
   int64_t s = ceil_div(target, base);

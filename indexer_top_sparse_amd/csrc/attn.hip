@@ -236,353 +236,8 @@ hipError_t launch_attn_f32(const AttnPlan& p, hipStream_t s) {
 }
 
 // =================================================================== bf16
-constexpr int kTT = 32;           // tokens per tile
-constexpr int kStages = 3;        // tiles in flight (register prefetch)
-constexpr int kMaxSplitTok = 2048;
-constexpr int kMlaHeads = 32;     // query heads per workgroup for latent rows
-
-template <int DQK, int DV, int HG, bool LATENT, int NW>
-struct AttnCfg {
-  static constexpr int kNT = 64 * NW;                   // threads
-  static constexpr int kRowK = DQK + 8;                 // LDS row stride (elements)
-  static constexpr int kRowV = LATENT ? kRowK : DV + 8;
-  static constexpr int kCprK = DQK * 2 / 16;            // 16-byte chunks per K row
-  static constexpr int kCprV = LATENT ? 0 : DV * 2 / 16;
-  static constexpr int kChunks = kTT * (kCprK + kCprV);
-  static constexpr int kNch = (kChunks + kNT - 1) / kNT;
-  static constexpr int kKS = DQK / 32;                  // QK k-steps
-  static constexpr int kMT = HG / 16;                   // head m-tiles
-  static constexpr int kNTQ = kTT / 16;                 // QK token n-tiles
-  static constexpr int kPairs = kMT * kNTQ;
-  static constexpr int kKSplit = NW / kPairs;           // waves sharing one S tile
-  static constexpr int kKSW = kKS / kKSplit;            // k-steps per wave
-  static constexpr int kWC = DV / NW;                   // PV columns per wave
-  static constexpr int kCPL = kWC / 16;                 // PV columns per lane
-  static constexpr int kTPR = kNT / HG;                 // softmax threads per row
-  static constexpr int kEPT = kTT / kTPR;               // softmax entries per thread
-  // S rows padded so the four 16-lane groups of an MFMA result write
-  // disjoint bank ranges
-  static constexpr int kSRow = kTT + 4;
-  static_assert(NW % kPairs == 0 && kKS % kKSplit == 0, "QK work split");
-  static_assert(kCPL == 2 || kCPL == 4 || kCPL == 8, "PV strip width");
-  static_assert(kTPR <= 64 && kEPT >= 1, "softmax split");
-};
-
-// Row pointer word: the 16-byte aligned address of the token's K row, with
-// bit 0 set when the slot is masked (then the address is a finite dummy row
-// so that every load in the pipeline is unconditional).
-template <int DQK, int DV, int HG, bool LATENT, int NW>
-__global__ __launch_bounds__(64 * NW) void attn_bf16_kernel(AttnPlan p) {
-  using C = AttnCfg<DQK, DV, HG, LATENT, NW>;
-  __shared__ __attribute__((aligned(16))) uint16_t ks_s[kTT * C::kRowK];
-  __shared__ __attribute__((aligned(16))) uint16_t vs_s[LATENT ? 8 : kTT * C::kRowV];
-  __shared__ float s_s[C::kKSplit * HG * C::kSRow];
-  __shared__ __attribute__((aligned(16))) uint16_t p_s[HG * (kTT + 8)];
-  __shared__ float alpha_s[HG];
-  __shared__ float m_s[HG];
-  __shared__ float l_s[HG];
-  __shared__ uint64_t rowp_s[kMaxSplitTok];
-
-  const sparse_attn_args& A = p.a;
-  // XCD-aware order: workgroup i runs on XCD i % 8, and the head groups of
-  // one (request, split) read the same KV rows, so they get ids that differ
-  // by multiples of 8 and are dispatched back to back on one XCD (one L2).
-  const int ngrp = (A.n_kv_heads == 1) ? A.n_q_heads / HG : A.n_kv_heads;
-  const int unit = (int)(blockIdx.x % 8) + 8 * (int)(blockIdx.x / (8 * ngrp));
-  const int grp = (int)(blockIdx.x / 8) % ngrp;
-  if (unit >= p.splits * A.batch) return;
-  const int split = unit % p.splits;
-  const int b = unit / p.splits;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wid = tid >> 6;
-  const int G = A.n_q_heads / A.n_kv_heads;
-  // head group: latent rows (one KV head, HG query heads per group) or one
-  // KV head per group with its G <= HG query heads (rows past G are padding)
-  const int kvh = (A.n_kv_heads == 1) ? 0 : grp;
-  const int head0 = (A.n_kv_heads == 1) ? grp * HG : grp * G;
-  const int greal = (A.n_kv_heads == 1) ? HG : G;
-  const int selrow_i = p.sel_heads == 1 ? 0 : kvh;
-  const int32_t* selrow = p.sel + ((int64_t)b * p.sel_heads + selrow_i) * p.k;
-  const int valid = valid_tokens(A, b);
-  const int tps = (p.k_tokens + p.splits - 1) / p.splits;
-  const int j0 = split * tps;
-  const int j1 = min(j0 + tps, p.k_tokens);
-  const int cnt = max(0, j1 - j0);
-  const int ntiles = (cnt + kTT - 1) / kTT;
-  const int64_t stage_base = ((int64_t)b * p.sel_heads + selrow_i) * p.k_tokens;
-  RowAddr ra{A};
-  const int64_t vdelta = LATENT ? 0 : (const char*)A.v_cache - (const char*)A.k_cache;
-
-  // ---- resolve every row of the split once (selection -> page / slot)
-  const uint64_t dummy =
-      ((uint64_t)(A.hot_slot ? (const char*)A.hot_kv + (int64_t)b * A.hot_stride_b * 2
-                             : (const char*)A.k_cache)) | 1ull;
-  for (int i = tid; i < cnt; i += C::kNT) {
-    const int j = j0 + i;
-    const int t = sel_token(selrow, j, p.sel_unit, valid);
-    rowp_s[i] = t >= 0 ? (uint64_t)ra.k_row(b, kvh, t, stage_base + j, p.staging, 2)
-                       : dummy;
-  }
-  __syncthreads();
-
-  // ---- q operands (A of QK): head 16*mt + (lane%16), dims 32s + 8(lane/16)
-  const int pair = wid % C::kPairs;
-  const int kpart = wid / C::kPairs;
-  const int qmt = pair / C::kNTQ;
-  const int qnt = pair % C::kNTQ;
-  bf16x8 qa[C::kKSW];
-  {
-    const int hr = qmt * 16 + (lane & 15);
-    const bool real = hr < greal;
-    const uint16_t* qp = (const uint16_t*)A.q + (int64_t)b * A.q_stride_b +
-                         (int64_t)(head0 + (real ? hr : 0)) * A.q_stride_h +
-                         32 * (kpart * C::kKSW) + 8 * (lane >> 4);
-#pragma unroll
-    for (int s = 0; s < C::kKSW; ++s) {
-      if (real) qa[s] = *(const bf16x8*)(qp + 32 * s);
-      else for (int e = 0; e < 8; ++e) qa[s][e] = (__bf16)0.f;
-    }
-  }
-
-  // ---- tile gather: kNch 16-byte chunks per thread, all loads unconditional.
-  // Chunk i of this thread is row crow[i] of the tile at byte offset
-  // coff[i] of that row's K (or, past the K chunks, V) data.
-  int crow[C::kNch];
-  int64_t coff[C::kNch];
-  int lofs[C::kNch];
-#pragma unroll
-  for (int i = 0; i < C::kNch; ++i) {
-    const int q = tid + i * C::kNT;
-    const int qc = q < C::kChunks ? q : C::kChunks - 1;
-    const bool isv = qc >= kTT * C::kCprK;
-    const int qq = isv ? qc - kTT * C::kCprK : qc;
-    const int cpr = isv ? C::kCprV : C::kCprK;
-    crow[i] = qq / cpr;
-    const int cc = qq % cpr;
-    coff[i] = (isv ? vdelta : 0) + 16 * cc;
-    // LDS destination: element offset in ks_s, or in vs_s with bit 30 set;
-    // -1 for the idle slots of the last round
-    lofs[i] = q < C::kChunks
-                  ? (isv ? (1 << 30) | (crow[i] * C::kRowV + 8 * cc) : crow[i] * C::kRowK + 8 * cc)
-                  : -1;
-  }
-  auto gather = [&](u32x4 (&pre)[C::kNch], int tile) __attribute__((always_inline)) {
-    uint64_t w[C::kNch];
-#pragma unroll
-    for (int i = 0; i < C::kNch; ++i) {
-      const int it = tile * kTT + crow[i];
-      w[i] = it < cnt ? rowp_s[it] : dummy;
-    }
-#pragma unroll
-    for (int i = 0; i < C::kNch; ++i)
-      pre[i] = *(gptr<const u32x4>)((const char*)(w[i] & ~15ull) + coff[i]);
-  };
-  auto commit = [&](const u32x4 (&pre)[C::kNch]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < C::kNch; ++i)
-      if (lofs[i] >= 0) {
-        uint16_t* dst = (lofs[i] & (1 << 30)) ? vs_s + (lofs[i] & ((1 << 30) - 1))
-                                               : ks_s + lofs[i];
-        *(u32x4*)dst = pre[i];
-      }
-  };
-
-  // ---- softmax row state (replicated across the kTPR threads of a row)
-  const int srow = tid / C::kTPR;
-  const int ssub = tid % C::kTPR;
-  float m_run = -__builtin_huge_valf();
-  float l_run = 0.f;
-
-  // ---- output accumulators: rows 16*mt + 4*(lane/16) + i, columns
-  // wid*kWC + kCPL*(lane%16) + nt
-  f32x4 o[C::kMT][C::kCPL];
-#pragma unroll
-  for (int mt = 0; mt < C::kMT; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < C::kCPL; ++nt)
-      for (int e = 0; e < 4; ++e) o[mt][nt][e] = 0.f;
-
-  auto process = [&](int tile) __attribute__((always_inline)) {
-    // ---- partial S = scale * q K^T over this wave's k-steps
-    {
-      f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-      const uint16_t* kr = ks_s + (16 * qnt + (lane & 15)) * C::kRowK +
-                           32 * (kpart * C::kKSW) + 8 * (lane >> 4);
-      bf16x8 kv[C::kKSW];
-#pragma unroll
-      for (int s = 0; s < C::kKSW; ++s) kv[s] = *(const bf16x8*)(kr + 32 * s);
-#pragma unroll
-      for (int s = 0; s < C::kKSW; ++s) {
-        if (s & 1) acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], kv[s], acc1, 0, 0, 0);
-        else acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], kv[s], acc0, 0, 0, 0);
-      }
-      const int colq = 16 * qnt + (lane & 15);
-      float* sp = s_s + kpart * HG * C::kSRow;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * qmt + 4 * (lane >> 4) + i;
-        sp[r * C::kSRow + colq] = acc0[i] + acc1[i];
-      }
-    }
-    __syncthreads();
-
-    // ---- online softmax over the tile
-    {
-      float sv[C::kEPT];
-      float sp[C::kKSplit][C::kEPT];
-      uint64_t rw[C::kEPT];
-#pragma unroll
-      for (int e = 0; e < C::kEPT; ++e) {
-        const int col = ssub * C::kEPT + e;
-        const int it = tile * kTT + col;
-        rw[e] = it < cnt ? rowp_s[it] : 1ull;
-#pragma unroll
-        for (int kp = 0; kp < C::kKSplit; ++kp) sp[kp][e] = s_s[(kp * HG + srow) * C::kSRow + col];
-      }
-      float tmax = -__builtin_huge_valf();
-#pragma unroll
-      for (int e = 0; e < C::kEPT; ++e) {
-        float v = 0.f;
-#pragma unroll
-        for (int kp = 0; kp < C::kKSplit; ++kp) v += sp[kp][e];
-        sv[e] = (rw[e] & 1ull) ? -__builtin_huge_valf() : v * A.sm_scale;
-        tmax = fmaxf(tmax, sv[e]);
-      }
-      static_assert(C::kTPR == 16, "softmax rows are 16-lane DPP rows");
-      tmax = row16_max(tmax);
-      const float m_new = fmaxf(m_run, tmax);
-      const bool none = (m_new == -__builtin_huge_valf());
-      const float alpha = none ? 1.f : __expf(m_run - m_new);
-      float psum = 0.f;
-#pragma unroll
-      for (int e = 0; e < C::kEPT; ++e) {
-        float pe = none ? 0.f : __expf(sv[e] - m_new);
-        __bf16 pb = (__bf16)pe;
-        psum += (float)pb;
-        p_s[srow * (kTT + 8) + ssub * C::kEPT + e] = __builtin_bit_cast(uint16_t, pb);
-      }
-      psum = row16_sum(psum);
-      l_run = alpha * l_run + psum;
-      m_run = m_new;
-      if (ssub == 0) alpha_s[srow] = alpha;
-    }
-    __syncthreads();
-
-    // ---- O = alpha * O + P V  (wave: all heads x kWC columns)
-    {
-      float al[C::kMT][4];
-#pragma unroll
-      for (int mt = 0; mt < C::kMT; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) al[mt][i] = alpha_s[16 * mt + 4 * (lane >> 4) + i];
-      bf16x8 pa[C::kMT];
-#pragma unroll
-      for (int mt = 0; mt < C::kMT; ++mt)
-        pa[mt] = *(const bf16x8*)(p_s + (16 * mt + (lane & 15)) * (kTT + 8) + 8 * (lane >> 4));
-      // V strip: tokens 8*(lane/16) + i, columns wid*kWC + kCPL*(lane%16) ..
-      const uint16_t* vbase = (LATENT ? ks_s : vs_s) + (8 * (lane >> 4)) * C::kRowV +
-                              wid * C::kWC + C::kCPL * (lane & 15);
-      constexpr int DW = C::kCPL / 2;  // dwords per token strip
-      uint32_t raw[8][DW];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint16_t* vp = vbase + i * C::kRowV;
-        if constexpr (DW == 4) {
-          uint4 v = *(const uint4*)vp;
-          raw[i][0] = v.x; raw[i][1] = v.y; raw[i][2] = v.z; raw[i][3] = v.w;
-        } else if constexpr (DW == 2) {
-          uint2 v = *(const uint2*)vp;
-          raw[i][0] = v.x; raw[i][1] = v.y;
-        } else {
-          raw[i][0] = *(const uint32_t*)vp;
-        }
-      }
-#pragma unroll
-      for (int mt = 0; mt < C::kMT; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < C::kCPL; ++nt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) o[mt][nt][i] *= al[mt][i];
-#pragma unroll
-      for (int nt = 0; nt < C::kCPL; ++nt) {
-        const uint32_t sel = (nt & 1) ? 0x07060302u : 0x05040100u;
-        uint32_t d[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          d[e] = __builtin_amdgcn_perm(raw[2 * e + 1][nt >> 1], raw[2 * e][nt >> 1], sel);
-        bf16x8 vb = __builtin_bit_cast(bf16x8, make_uint4(d[0], d[1], d[2], d[3]));
-#pragma unroll
-        for (int mt = 0; mt < C::kMT; ++mt)
-          o[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[mt], vb, o[mt][nt], 0, 0, 0);
-      }
-    }
-  };
-
-  // ---- pipeline: tile t is gathered kStages-1 tiles ahead into buffer
-  // t % kStages; the loop runs whole groups of kStages tiles (a tile past
-  // the split is fully masked and leaves the state unchanged, and its loads
-  // hit the dummy row).
-  static_assert(kStages == 3, "the pipeline below is written for 3 stages");
-  u32x4 pre0[C::kNch], pre1[C::kNch], pre2[C::kNch];
-  const int groups = (ntiles + kStages - 1) / kStages;
-  gather(pre0, 0);
-  gather(pre1, 1);
-  for (int g = 0; g < groups; ++g) {
-    const int t = g * kStages;
-    gather(pre2, t + 2);
-    __syncthreads();  // the previous tile's LDS readers are done
-    commit(pre0);
-    __syncthreads();
-    process(t);
-    gather(pre0, t + 3);
-    __syncthreads();
-    commit(pre1);
-    __syncthreads();
-    process(t + 1);
-    gather(pre1, t + 4);
-    __syncthreads();
-    commit(pre2);
-    __syncthreads();
-    process(t + 2);
-  }
-
-  // ---- epilogue
-  if (ssub == 0) {
-    m_s[srow] = m_run;
-    l_s[srow] = l_run;
-  }
-  __syncthreads();
-  const int Hq = A.n_q_heads;
-#pragma unroll
-  for (int mt = 0; mt < C::kMT; ++mt) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * mt + 4 * (lane >> 4) + i;
-      if (r >= greal) continue;
-      const int64_t oh = (int64_t)b * Hq + head0 + r;
-      const float l = l_s[r];
-      const float inv = l > 0.f ? 1.f / l : 0.f;
-#pragma unroll
-      for (int nt = 0; nt < C::kCPL; ++nt) {
-        const int col = wid * C::kWC + C::kCPL * (lane & 15) + nt;
-        if (p.splits == 1) p.out[oh * DV + col] = o[mt][nt][i] * inv;
-        else p.part[(oh * p.splits + split) * (DV + 4) + col] = o[mt][nt][i];
-      }
-    }
-  }
-  if (tid < greal && tid < HG) {
-    const int64_t oh = (int64_t)b * Hq + head0 + tid;
-    const float m = m_s[tid], l = l_s[tid];
-    if (p.splits == 1) {
-      if (p.lse) p.lse[oh] = l > 0.f ? m + __logf(l) : -__builtin_huge_valf();
-    } else {
-      float* pp = p.part + (oh * p.splits + split) * (DV + 4);
-      pp[DV] = m;
-      pp[DV + 1] = l;
-    }
-  }
-}
+constexpr int kTT = 32;            // tokens per tile
+constexpr int kMaxSplitTok = 2048;  // row-table entries of one split
 
 // ============================================================ latent (MLA)
 // Latent rows (d_qk 576, values = the first 512 dims of the same row), one
@@ -904,6 +559,245 @@ __global__ __launch_bounds__(kMlaThreads, 1) void attn_mla_kernel(AttnPlan p) {
   }
 }
 
+// ==================================================================== GQA
+// d_qk = d_v = 128, up to 16 query heads per KV head, bf16.  One workgroup of
+// kGqaWaves waves per (request, KV head, token split); the waves take the
+// split's 32-token tiles in turn, each wave with its own online-softmax
+// state, and merge through LDS once at the end, so the tile loop has no
+// barrier.  Per tile a wave computes
+//   S^T[32 tokens x 16 heads] = K Q^T  (A = K rows loaded from global memory
+//       straight into the MFMA layout, B = q in registers; heads past the
+//       group's G are zero),
+//   the online softmax per head in the base-2 domain, with the lazy
+//       rescale of the latent kernel (lane l holds head l % 16),
+//   O^T[128 x 16] += V^T P^T  (A = V^T read from the wave's LDS copy of the
+//       tile with ds_read_b64_tr_b16, B = the lane's own probabilities, in
+//       the token order of the latent kernel).
+// The K and V loads of a wave's next tile are in flight while it works on
+// the current one.
+constexpr int kGqaWaves = 4;
+constexpr int kGqaRowV = 128 + 8;  // LDS row stride of a V tile (elements)
+
+struct GqaTile {
+  u32x4 k[2][4];  // K[token 16 mt + n][32 s + 8 g ..], lane (g, n)
+  u32x4 v[8];     // V row (lane / 16) + 4 u, 16-byte chunk lane % 16
+};
+
+__global__ __launch_bounds__(64 * kGqaWaves) void attn_gqa_kernel(AttnPlan p) {
+  __shared__ __attribute__((aligned(16))) uint16_t vs_s[kGqaWaves][kTT * kGqaRowV];
+  __shared__ uint64_t rowp_s[kMaxSplitTok];
+  __shared__ uint32_t vmask_s[kMaxSplitTok / kTT];
+  __shared__ float ml_s[kGqaWaves][16][2];
+
+  const sparse_attn_args& A = p.a;
+  const int ngrp = A.n_kv_heads;
+  const int unit = (int)(blockIdx.x % 8) + 8 * (int)(blockIdx.x / (8 * ngrp));
+  const int kvh = (int)(blockIdx.x / 8) % ngrp;
+  if (unit >= p.splits * A.batch) return;
+  const int split = unit % p.splits;
+  const int b = unit / p.splits;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wid = tid >> 6;
+  const int g = lane >> 4;
+  const int n = lane & 15;
+  const int G = A.n_q_heads / A.n_kv_heads;
+  const int head0 = kvh * G;
+  const int selrow_i = p.sel_heads == 1 ? 0 : kvh;
+  const int32_t* selrow = p.sel + ((int64_t)b * p.sel_heads + selrow_i) * p.k;
+  const int valid = valid_tokens(A, b);
+  const int tps = (p.k_tokens + p.splits - 1) / p.splits;
+  const int j0 = split * tps;
+  const int j1 = min(j0 + tps, p.k_tokens);
+  const int cnt = max(0, j1 - j0);
+  const int ntiles = (cnt + kTT - 1) / kTT;
+  RowAddr ra{A};
+  const int64_t vdelta = (const char*)A.v_cache - (const char*)A.k_cache;
+
+  // q of head n as the B operand: B[k = 32 s + 8 g + e][n]; zero past G
+  bf16x8 qb[4];
+  {
+    const bool real = n < G;
+    const uint16_t* qp = (const uint16_t*)A.q + (int64_t)b * A.q_stride_b +
+                         (int64_t)(head0 + (real ? n : 0)) * A.q_stride_h + 8 * g;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const bf16x8 x = *(const bf16x8*)(qp + 32 * s);
+      qb[s] = real ? x : bf16x8{};
+    }
+  }
+
+  // row table (K rows; masked positions point at a finite dummy row) and
+  // the valid-token bits of every tile
+  const uint64_t dummy = (uint64_t)(const char*)A.k_cache;
+  for (int base = 0; base < ntiles * kTT; base += 64 * kGqaWaves) {
+    const int i = base + tid;
+    int t = -1;
+    if (i < cnt) t = sel_token(selrow, j0 + i, p.sel_unit, valid);
+    if (i < ntiles * kTT)
+      rowp_s[i] = t >= 0 ? (uint64_t)ra.k_row(b, kvh, t, 0, nullptr, 2) : dummy;
+    const uint64_t bal = __builtin_amdgcn_ballot_w64(t >= 0);
+    const int tile = (base >> 5) + 2 * wid;  // lanes 0..31: tile, 32..63: tile + 1
+    if (lane == 0 && tile < ntiles) vmask_s[tile] = (uint32_t)bal;
+    if (lane == 0 && tile + 1 < ntiles) vmask_s[tile + 1] = (uint32_t)(bal >> 32);
+  }
+  __syncthreads();
+
+  auto load = [&](GqaTile& T, int tile) __attribute__((always_inline)) {
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const char* kr = (const char*)rowp_s[tile * kTT + 16 * mt + n] + 16 * g;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) T.k[mt][s] = *(gptr<const u32x4>)(kr + 64 * s);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      T.v[u] = *(gptr<const u32x4>)((const char*)rowp_s[tile * kTT + g + 4 * u] + vdelta + 16 * n);
+  };
+
+  const float qk_scale = A.sm_scale * kLog2e;
+  const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3F803F80u);
+  float m_run = -__builtin_huge_valf();  // base-2 reference max of head n
+  float l_run = 0.f;
+  f32x4 o[8];  // O^T: o[mc][i] = column 16 mc + 4 g + i of head n
+#pragma unroll
+  for (int mc = 0; mc < 8; ++mc) o[mc] = f32x4{0.f, 0.f, 0.f, 0.f};
+  uint16_t* vs = vs_s[wid];
+
+  auto process = [&](const GqaTile& T, int tile) __attribute__((always_inline)) {
+    f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, T.k[0][s]), qb[s], a0, 0, 0, 0);
+      a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, T.k[1][s]), qb[s], a1, 0, 0, 0);
+    }
+    // the tile's V rows into this wave's LDS copy (read back transposed below)
+#pragma unroll
+    for (int u = 0; u < 8; ++u) *(u32x4*)(vs + (g + 4 * u) * kGqaRowV + 8 * n) = T.v[u];
+    float sv[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sv[i] = a0[i] * qk_scale;
+      sv[4 + i] = a1[i] * qk_scale;
+    }
+    const uint32_t vm = __builtin_amdgcn_readfirstlane(vmask_s[tile]);
+    if (vm != 0xFFFFFFFFu) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (!((vm >> (16 * (e >> 2) + 4 * g + (e & 3))) & 1u)) sv[e] = -__builtin_huge_valf();
+    }
+    float tmax = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                       fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+    tmax = fmaxf(tmax, xlane16(tmax));
+    tmax = fmaxf(tmax, swap_halves(tmax));
+    constexpr float kSlack = 8.0f;
+    if (__builtin_amdgcn_ballot_w64(tmax > m_run + kSlack)) {
+      const float m_new = fmaxf(m_run, tmax);
+      const float alpha =
+          (m_run == -__builtin_huge_valf()) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+#pragma unroll
+      for (int mc = 0; mc < 8; ++mc) o[mc] *= alpha;
+      l_run *= alpha;
+      m_run = m_new;
+    }
+    const bool none = (m_run == -__builtin_huge_valf());
+    float psum = 0.f;
+    uint32_t pk[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float p0 = none ? 0.f : __builtin_amdgcn_exp2f(sv[2 * e] - m_run);
+      const float p1 = none ? 0.f : __builtin_amdgcn_exp2f(sv[2 * e + 1] - m_run);
+      const bf16x2 pp = bf16x2{(__bf16)p0, (__bf16)p1};
+      psum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, psum, false);
+      pk[e] = __builtin_bit_cast(uint32_t, pp);
+    }
+    psum += xlane16(psum);
+    psum += swap_halves(psum);
+    l_run += psum;
+    // B operand of P V: k = 8g + e  <->  token (e < 4 ? 4g + e : 16 + 4g + e - 4)
+    const bf16x8 pb = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+    // A operand, m-tile mc: lane (g, n) needs column 16 mc + n of those
+    // eight tokens; lane n of each group addresses token row n / 4 of the
+    // four and columns 4 (n % 4) .. +3
+    const uint16_t* vb = vs + (4 * g + (n >> 2)) * kGqaRowV + 4 * (n & 3);
+#pragma unroll
+    for (int mc = 0; mc < 8; ++mc) {
+      const s16x4 r0 = lds_read_tr16(vb + 16 * mc);
+      const s16x4 r1 = lds_read_tr16(vb + 16 * kGqaRowV + 16 * mc);
+      const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7));
+      o[mc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, o[mc], 0, 0, 0);
+    }
+  };
+
+  // this wave's tiles: wid, wid + kGqaWaves, ...; the next one in flight
+  {
+    GqaTile ta, tb;
+    int t = wid;
+    if (t < ntiles) load(ta, t);
+    while (t < ntiles) {
+      if (t + kGqaWaves < ntiles) load(tb, t + kGqaWaves);
+      process(ta, t);
+      t += kGqaWaves;
+      if (t >= ntiles) break;
+      if (t + kGqaWaves < ntiles) load(ta, t + kGqaWaves);
+      process(tb, t);
+      t += kGqaWaves;
+    }
+  }
+
+  // ---- merge the waves: M = max m_w, f_w = 2^(m_w - M), L = sum l_w f_w,
+  // O = sum f_w O_w (through LDS, reusing the V copies)
+  if (g == 0) {
+    ml_s[wid][n][0] = m_run;
+    ml_s[wid][n][1] = l_run;
+  }
+  __syncthreads();
+  float M = -__builtin_huge_valf();
+#pragma unroll
+  for (int w = 0; w < kGqaWaves; ++w)
+    if (ml_s[w][n][1] > 0.f) M = fmaxf(M, ml_s[w][n][0]);
+  float L = 0.f, f_own = 0.f;
+#pragma unroll
+  for (int w = 0; w < kGqaWaves; ++w) {
+    const float lw = ml_s[w][n][1];
+    const float fw = lw > 0.f ? __builtin_amdgcn_exp2f(ml_s[w][n][0] - M) : 0.f;
+    L += lw * fw;
+    if (w == wid) f_own = fw;
+  }
+  f32x4* os = (f32x4*)vs;  // 8 KiB of this wave's region: slot mc * 64 + lane
+#pragma unroll
+  for (int mc = 0; mc < 8; ++mc) os[mc * 64 + lane] = o[mc] * f_own;
+  __syncthreads();
+  // thread (wave wid, lane) sums m-tiles 2 wid and 2 wid + 1 of that lane
+  const int64_t oh = (int64_t)b * A.n_q_heads + head0 + n;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int mc = 2 * wid + h;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < kGqaWaves; ++w) acc += ((const f32x4*)vs_s[w])[mc * 64 + lane];
+    if (n < G) {
+      const int col = 16 * mc + 4 * g;
+      if (p.splits == 1) {
+        const float inv = L > 0.f ? 1.f / L : 0.f;
+        *(f32x4*)(p.out + oh * 128 + col) = acc * inv;
+      } else {
+        *(f32x4*)(p.part + (oh * p.splits + split) * (128 + 4) + col) = acc;
+      }
+    }
+  }
+  if (wid == 0 && g == 0 && n < G) {
+    const float m_nat = M * kLn2;  // natural-log domain of the combine
+    if (p.splits == 1) {
+      if (p.lse) p.lse[oh] = L > 0.f ? m_nat + __logf(L) : -__builtin_huge_valf();
+    } else {
+      float* pp = p.part + (oh * p.splits + split) * (128 + 4);
+      pp[128] = m_nat;
+      pp[129] = L;
+    }
+  }
+}
+
 hipError_t launch_attn_bf16(const AttnPlan& p, hipStream_t s) {
   const sparse_attn_args& a = p.a;
   // 8 * groups * ceil(units / 8) workgroup ids (the kernel decodes them)
@@ -916,7 +810,7 @@ hipError_t launch_attn_bf16(const AttnPlan& p, hipStream_t s) {
   } else if (a.d_qk == 128 && a.d_v == 128 && a.v_cache != nullptr) {
     const int groups = a.n_kv_heads;
     dim3 grid((unsigned)(8 * groups * rounds), 1, 1);
-    attn_bf16_kernel<128, 128, 16, false, 4><<<grid, 256, 0, s>>>(p);
+    attn_gqa_kernel<<<grid, 64 * kGqaWaves, 0, s>>>(p);
   } else {
     return hipErrorInvalidValue;
   }
