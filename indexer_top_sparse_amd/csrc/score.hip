@@ -701,7 +701,10 @@ int score_part_span(const sparse_index_args& a) {
     case SPARSE_SCORE_LIGHTNING:
       return (lightning_long(a) ? kLtLong : kLtShort) * kLtStride;
     default:
-      return 0;  // bit-plane parts take passes grid-stride
+      // a part holds at most one pass, so bitplane_parts gives one part per
+      // pass and workgroup x scores the contiguous tokens of pass x
+      static_assert(kBpMaxPasses == 1, "one pass per histogram part");
+      return kBpPassTok;
   }
 }
 
