@@ -593,19 +593,21 @@ hipError_t launch_read_depth(const sparse_index_args* a, int8_t* depth, int32_t*
 
 // ========================================================================
 // Fathom plane-prefix scan.  A thread owns one 32-bit word column of a
-// (request, KV head): 32 consecutive tokens.  For each read plane (c, j)
-// from the list read_depth_kernel wrote it loads that plane's word
-// (coalesced across the workgroup) and adds the plane weight W_{c,j} to the
-// tokens whose bit is set; the bit becomes an all-ones or all-zero mask of
-// the weight's bits (sign-extending bit field), so a token costs one
-// extract, one AND and one add per plane.  Loads run kBpUnroll planes
-// ahead of their use.
+// (request, KV head): 32 consecutive tokens.  The read planes (c, j) from
+// the list read_depth_kernel wrote are taken four at a time: the workgroup
+// first tabulates, for every group of four planes, the 16 sums of their
+// weights W_{c,j} over each subset of the group.  Per group a thread loads
+// the four plane words (coalesced across the workgroup), bit-slices them
+// into 4-bit indices -- nibble i of word q holds bit 8q + i of the four
+// planes, spread by three shift-or-mask steps per byte -- and adds the
+// table entry of each token's index: one extract, one LDS read and one add
+// per token and group instead of per token and plane.  The next four
+// groups are in flight while four are processed.
 // ========================================================================
 constexpr int kBpThreads = 1024;
 constexpr int kBpPassTok = kBpThreads * 32;             // 32768 tokens per workgroup pass
 constexpr int kBpMaxPasses = kHistPartMax / kBpPassTok;  // per workgroup (histogram part)
-constexpr int kBpUnroll = 4;
-static_assert(kPlaneBatch % kBpUnroll == 0, "padded plane list");
+static_assert(kPlaneBatch % 8 == 0, "padded plane list: whole pairs of four-plane groups");
 
 int bitplane_parts(const sparse_index_args& a) {
   const int passes = (a.n + kBpPassTok - 1) / kBpPassTok;
@@ -618,12 +620,21 @@ int bitplane_parts(const sparse_index_args& a) {
   return std::max(parts, 1);
 }
 
+// bit i of byte x -> bit 4i
+__device__ __forceinline__ uint32_t spread_nibbles(uint32_t x) {
+  x = (x | (x << 12)) & 0x000F000Fu;
+  x = (x | (x << 6)) & 0x03030303u;
+  x = (x | (x << 3)) & 0x11111111u;
+  return x;
+}
+
 __global__ __launch_bounds__(kBpThreads) void score_bitplane_kernel(
     sparse_index_args a, const int32_t* plist, const float* pwl, const int32_t* npl,
     const float* score_c, float* __restrict__ scores, uint32_t* hist, int n_units) {
   __shared__ uint32_t hist_s[kHistBins];
   __shared__ int32_t pl_s[512];
   __shared__ float pw_s[512];
+  __shared__ float lut_s[512 / 4 * 16];  // [group][subset of its four planes]
   LdsHist lh{hist_s};
   const int h = blockIdx.y;
   const int b = blockIdx.z;
@@ -642,6 +653,16 @@ __global__ __launch_bounds__(kBpThreads) void score_bitplane_kernel(
   }
   if (hist) lh.clear(kBpThreads);  // (ends with a barrier)
   else __syncthreads();
+  // subset sums of each group, in plane order
+  for (int e = threadIdx.x; e < npad / 4 * 16; e += kBpThreads) {
+    const int g = e >> 4, m = e & 15;
+    float x = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if ((m >> k) & 1) x += pw_s[4 * g + k];
+    lut_s[e] = x;
+  }
+  __syncthreads();
   const float c0 = score_c[bh];
   const uint32_t* planes = a.planes + bh * 4 * D * (int64_t)nw;
   float* srow = scores + bh * n_units;
@@ -652,21 +673,42 @@ __global__ __launch_bounds__(kBpThreads) void score_bitplane_kernel(
     float acc[32];
 #pragma unroll
     for (int i = 0; i < 32; ++i) acc[i] = c0;
-    for (int p0 = 0; p0 < npad; p0 += kBpUnroll) {
-      uint32_t wd[kBpUnroll];
+    auto load_group = [&](uint32_t (&wd)[4], int p0) __attribute__((always_inline)) {
 #pragma unroll
-      for (int k = 0; k < kBpUnroll; ++k)
+      for (int k = 0; k < 4; ++k)
         wd[k] = __builtin_nontemporal_load(planes + (int64_t)pl_s[p0 + k] * nw + wc);
+    };
+    auto add_group = [&](const uint32_t (&wd)[4], int p0) __attribute__((always_inline)) {
+      const float* lut = lut_s + (p0 >> 2) * 16;
 #pragma unroll
-      for (int k = 0; k < kBpUnroll; ++k) {
-        const uint32_t wb = __float_as_uint(pw_s[p0 + k]);
+      for (int q = 0; q < 4; ++q) {
+        uint32_t nb = spread_nibbles(__builtin_amdgcn_ubfe(wd[0], 8 * q, 8));
 #pragma unroll
-        for (int i = 0; i < 32; ++i) {
-          // bit i of the word, sign-extended: all ones or zero
-          const uint32_t m = (uint32_t)__builtin_amdgcn_sbfe((int)wd[k], i, 1);
-          acc[i] += __uint_as_float(wb & m);
-        }
+        for (int k = 1; k < 4; ++k)
+          nb |= spread_nibbles(__builtin_amdgcn_ubfe(wd[k], 8 * q, 8)) << k;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[8 * q + i] += lut[__builtin_amdgcn_ubfe(nb, 4 * i, 4)];
       }
+    };
+    // four groups per step, the next four in flight (npad is a multiple of
+    // 8, so the last step may hold only two)
+    constexpr int QG = 4;
+    uint32_t cur[QG][4];
+#pragma unroll
+    for (int gq = 0; gq < QG; ++gq)
+      if (4 * gq < npad) load_group(cur[gq], 4 * gq);
+    for (int p0 = 0; p0 < npad; p0 += 4 * QG) {
+      uint32_t nxt[QG][4];
+#pragma unroll
+      for (int gq = 0; gq < QG; ++gq)
+        if (p0 + 4 * QG + 4 * gq < npad) load_group(nxt[gq], p0 + 4 * QG + 4 * gq);
+#pragma unroll
+      for (int gq = 0; gq < QG; ++gq)
+        if (p0 + 4 * gq < npad) add_group(cur[gq], p0 + 4 * gq);
+#pragma unroll
+      for (int gq = 0; gq < QG; ++gq)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) cur[gq][k] = nxt[gq][k];
     }
     if (w < nw) {
 #pragma unroll
