@@ -120,6 +120,34 @@ __device__ __forceinline__ int wave_sum(int x) {
   return __builtin_amdgcn_readlane(wave_incl_scan(x), 63);
 }
 
+// Value of lane l ^ m (m a power of two below 64, known at compile time
+// once the caller's loop is unrolled): quad permutes for 1 and 2, a
+// half-row mirror then a quad reverse for 4, a row mirror then a half-row
+// mirror for 8, and the 16- and 32-lane swaps.
+__device__ __forceinline__ uint32_t lane_xor_u32(uint32_t v, int m) {
+  const int x = (int)v;
+  switch (m) {
+    case 1: return (uint32_t)__builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false);
+    case 2: return (uint32_t)__builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false);
+    case 4: {
+      const int y = __builtin_amdgcn_update_dpp(0, x, 0x141, 0xF, 0xF, false);
+      return (uint32_t)__builtin_amdgcn_update_dpp(0, y, 0x1B, 0xF, 0xF, false);
+    }
+    case 8: {
+      const int y = __builtin_amdgcn_update_dpp(0, x, 0x140, 0xF, 0xF, false);
+      return (uint32_t)__builtin_amdgcn_update_dpp(0, y, 0x141, 0xF, 0xF, false);
+    }
+    case 16: {
+      auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+      return (threadIdx.x & 16) ? r[0] : r[1];
+    }
+    default: {
+      auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+      return (threadIdx.x & 32) ? r[0] : r[1];
+    }
+  }
+}
+
 // ---------------------------------------------------------------- block scan
 // Inclusive prefix sum over a block of NT threads (NT multiple of 64).
 // `lds` must hold NT/64 + 1 ints.  Returns the inclusive sum for the thread

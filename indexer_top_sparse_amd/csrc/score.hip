@@ -500,6 +500,15 @@ __global__ __launch_bounds__(kDepthThreads) void read_depth_kernel(
   const int c = tid >> 2;
   const int j = tid & 3;
   const int64_t hd = ((int64_t)b * Hkv + h) * D;
+  // every global input first (one round trip): this thread's channel c
+  // (variance, or the given depth) and, for tid < D, channel tid's cell and
+  // zero point
+  const bool fixed = a.depth_in != nullptr;
+  const float var_c = (!fixed && c < D) ? a.chan_var[hd + c] : 0.f;
+  const int din_c = (fixed && c < D) ? (int)a.depth_in[hd + c] : 0;
+  const float cell_c = c < D ? a.chan_scale[hd + c] : 0.f;
+  const float cell_t = tid < D ? a.chan_scale[hd + tid] : 0.f;
+  const float zero_t = tid < D ? a.chan_zero[hd + tid] : 0.f;
   if (tid < D) {
     const uint16_t* q0 = (const uint16_t*)a.q + (int64_t)b * a.q_stride_b +
                          (int64_t)(h * G) * a.q_stride_h;
@@ -509,34 +518,46 @@ __global__ __launch_bounds__(kDepthThreads) void read_depth_kernel(
     qbar_s[tid] = acc;
   }
   __syncthreads();
-  if (a.depth_in == nullptr && c < D) {
+  if (!fixed && c < D) {
     double qb = qbar_s[c];
-    double imp = __dmul_rn(__dmul_rn(qb, qb), (double)a.chan_var[hd + c]);
+    double imp = __dmul_rn(__dmul_rn(qb, qb), (double)var_c);
     gain_s[tid] = ldexp(imp, -2 * j);
   }
   __syncthreads();
-  if (a.depth_in) {
+  if (fixed) {
     // a fixed allocation from the caller: planes j < t_c of channel c
-    const int tc = c < D ? min(max((int)a.depth_in[hd + c], 0), 4) : 0;
+    const int tc = c < D ? min(max(din_c, 0), 4) : 0;
     taken_s[tid] = j < tc;
     __syncthreads();
   } else {
   // Rank every gain in the total order (gain desc, channel asc, plane asc)
   // -- index order tid = 4c + j is (channel, plane) ascending -- with a
   // bitonic sort of (gain, index) pairs: position r of the sorted list holds
-  // the gain of rank r.  Slots past 4D hold -1 (below every gain).
+  // the gain of rank r.  Slots past 4D hold -1 (below every gain).  Steps
+  // between lanes of one wave exchange through DPP and lane swaps; only the
+  // six steps that cross waves go through LDS and barriers.
   {
     double key = c < D ? gain_s[tid] : -1.0;
     int id = tid;
+#pragma unroll
     for (int k = 2; k <= kDepthThreads; k <<= 1) {
+#pragma unroll
       for (int jj = k >> 1; jj > 0; jj >>= 1) {
-        __syncthreads();
-        gain_s[tid] = key;
-        taken_s[tid] = id;
-        __syncthreads();
         const int o = tid ^ jj;
-        const double ko = gain_s[o];
-        const int io = taken_s[o];
+        double ko;
+        int io;
+        if (jj >= kWave) {  // partner in another wave: through LDS
+          __syncthreads();
+          gain_s[tid] = key;
+          taken_s[tid] = id;
+          __syncthreads();
+          ko = gain_s[o];
+          io = taken_s[o];
+        } else {  // partner in this wave: DPP / lane swaps, no barrier
+          const uint2 kb = __builtin_bit_cast(uint2, key);
+          ko = __builtin_bit_cast(double, make_uint2(lane_xor_u32(kb.x, jj), lane_xor_u32(kb.y, jj)));
+          io = (int)lane_xor_u32((uint32_t)id, jj);
+        }
         const bool mine_first = (key > ko) || (key == ko && id < io);
         // the lower slot of an ascending block keeps the earlier element
         const bool keep_first = ((tid & k) == 0) == (tid < o);
@@ -554,9 +575,7 @@ __global__ __launch_bounds__(kDepthThreads) void read_depth_kernel(
             taken_s[4 * tid + 3];
     depth[hd + tid] = (int8_t)t;
     double qb = qbar_s[tid];
-    double cell = (double)a.chan_scale[hd + tid];
-    double zero = (double)a.chan_zero[hd + tid];
-    cterm_s[tid] = qb * (zero + cell * ldexp(1.0, 3 - t));
+    cterm_s[tid] = qb * ((double)zero_t + (double)cell_t * ldexp(1.0, 3 - t));
   }
   if (plist) {
     // read planes in (channel, plane) order with the weight of their bit
@@ -564,9 +583,8 @@ __global__ __launch_bounds__(kDepthThreads) void read_depth_kernel(
     const int incl = block_inclusive_scan<kDepthThreads>(taken, scan_s, &total);
     if (taken) {
       const double qb = qbar_s[c];
-      const double cell = (double)a.chan_scale[hd + c];
       plist[hd * 4 + incl - 1] = tid;
-      pwl[hd * 4 + incl - 1] = (float)(qb * cell * ldexp(1.0, 3 - j));
+      pwl[hd * 4 + incl - 1] = (float)(qb * (double)cell_c * ldexp(1.0, 3 - j));
     }
     if (tid == 0) npl[(int64_t)b * Hkv + h] = total;
     // pad the list to a multiple of kPlaneBatch with weightless plane 0
@@ -577,10 +595,13 @@ __global__ __launch_bounds__(kDepthThreads) void read_depth_kernel(
     }
   }
   __syncthreads();
-  if (score_c && tid == 0) {
-    double s = 0.0;
-    for (int i = 0; i < D; ++i) s += cterm_s[i];
-    score_c[(int64_t)b * Hkv + h] = (float)s;
+  // sum_c cterm_c as a fixed pairwise tree over the 128 channels
+  if (score_c) {
+    for (int w = D / 2; w >= 1; w >>= 1) {
+      if (tid < w) cterm_s[tid] += cterm_s[tid + w];
+      __syncthreads();
+    }
+    if (tid == 0) score_c[(int64_t)b * Hkv + h] = (float)cterm_s[0];
   }
 }
 
