@@ -235,8 +235,9 @@ hipError_t launch_topk_filter(const TopkPlan& p, hipStream_t s) {
 // contiguous candidate list, so the candidates are written in index order
 // straight to their final place.  Part 0 stores b*, the units above it and
 // the row's candidate count for the select.
-// NT threads, PER units per thread and pass: 512 x 16 for long parts,
-// 256 x 16 or 256 x 8 for parts of at most 4096 or 2048 units.
+// NT threads, PER units per thread and pass: 1024 x 16 for parts of more
+// than 8192 units, 512 x 16 down to 4097, 256 x 16 or 256 x 8 for parts of
+// at most 4096 or 2048 units.
 
 // (counts stay below 2^31)
 __device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t x, int) {
@@ -375,14 +376,16 @@ __global__ __launch_bounds__(NT) void topk_filter_fused_kernel(TopkPlan p) {
   int32_t* ci = p.cand_idx + (int64_t)r * p.n_units;
   int carry = (int)cnt_s[q0];
   for (int base = lo; base < hi; base += kFfPass) {
-    if (base != lo) load_raw(base);
     const int u0 = base + kFfPer * tid;
     uint32_t keys[kFfPer];
+#pragma unroll
+    for (int i = 0; i < kFfPer; ++i) keys[i] = score_key(raw[i]);
+    // the next pass's scores are in flight while this one is compacted
+    if (base + kFfPass < hi) load_raw(base + kFfPass);
     uint32_t flags = 0;
     int n_t = 0;
 #pragma unroll
     for (int i = 0; i < kFfPer; ++i) {
-      keys[i] = score_key(raw[i]);
       if (u0 + i < hi && (keys[i] >> 20) >= bstar) {
         flags |= 1u << i;
         ++n_t;
@@ -405,7 +408,8 @@ __global__ __launch_bounds__(NT) void topk_filter_fused_kernel(TopkPlan p) {
 
 hipError_t launch_topk_filter_fused(const TopkPlan& p, hipStream_t s) {
   dim3 grid(p.parts, p.rows);
-  if (p.part_span > 4096) topk_filter_fused_kernel<512, 16><<<grid, 512, 0, s>>>(p);
+  if (p.part_span > 8192) topk_filter_fused_kernel<1024, 16><<<grid, 1024, 0, s>>>(p);
+  else if (p.part_span > 4096) topk_filter_fused_kernel<512, 16><<<grid, 512, 0, s>>>(p);
   else if (p.part_span > 2048) topk_filter_fused_kernel<256, 16><<<grid, 256, 0, s>>>(p);
   else topk_filter_fused_kernel<256, 8><<<grid, 256, 0, s>>>(p);
   return hipGetLastError();
