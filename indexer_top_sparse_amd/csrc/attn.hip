@@ -298,7 +298,8 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const uint16_t* p) {
 __global__ __launch_bounds__(kMlaThreads, 1) void attn_mla_kernel(AttnPlan p) {
   __shared__ __attribute__((aligned(16))) uint16_t ks_s[3][kTT * kMlaRow];
   // probabilities of a tile as the P V waves' B operands, [buffer][head block][lane]
-  __shared__ __attribute__((aligned(16))) bf16x8 pb_s[2][4][64];
+  // [buffer][high part, residual][head block][lane]
+  __shared__ __attribute__((aligned(16))) bf16x8 pb_s[2][2][4][64];
   __shared__ float alpha_s[2][4][16];  // rescale factor of each head's O for that tile
   __shared__ float ml_s[kMlaHeadsWG][2];
   __shared__ uint64_t rowp_s[kMaxSplitTok + kMlaPad];
@@ -405,7 +406,6 @@ __global__ __launch_bounds__(kMlaThreads, 1) void attn_mla_kernel(AttnPlan p) {
     const float qk_scale = A.sm_scale * kLog2e;
     float m_run = -__builtin_huge_valf();  // base-2 reference max
     float l_run = 0.f;
-    const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3F803F80u);
     // S^T[32 tokens x 16 heads] of one tile, online softmax, probabilities
     // into LDS
     auto scores = [&](int tile, int buf, int sb) __attribute__((always_inline)) {
@@ -446,20 +446,24 @@ __global__ __launch_bounds__(kMlaThreads, 1) void attn_mla_kernel(AttnPlan p) {
       if (g == 0) alpha_s[sb][wid][n] = alpha;
       const bool none = (m_run == -__builtin_huge_valf());
       float psum = 0.f;
-      uint32_t pk[4];
+      uint32_t ph[4], pl[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float p0 = none ? 0.f : __builtin_amdgcn_exp2f(sv[2 * e] - m_run);
         const float p1 = none ? 0.f : __builtin_amdgcn_exp2f(sv[2 * e + 1] - m_run);
-        const bf16x2 pp = bf16x2{(__bf16)p0, (__bf16)p1};
-        psum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, psum, false);
-        pk[e] = __builtin_bit_cast(uint32_t, pp);
+        psum += p0 + p1;
+        const bf16x2 hi = bf16x2{(__bf16)p0, (__bf16)p1};
+        const bf16x2 lo = bf16x2{(__bf16)(p0 - (float)hi[0]), (__bf16)(p1 - (float)hi[1])};
+        ph[e] = __builtin_bit_cast(uint32_t, hi);
+        pl[e] = __builtin_bit_cast(uint32_t, lo);
       }
       psum += xlane16(psum);
       psum += swap_halves(psum);
       l_run += psum;
-      // B operand of P V: k = 8g + e  <->  token (e < 4 ? 4g + e : 16 + 4g + e - 4)
-      pb_s[sb][wid][lane] = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+      // B operands of P V, high part and residual (p = hi + lo to 2^-17):
+      // k = 8g + e  <->  token (e < 4 ? 4g + e : 16 + 4g + e - 4)
+      pb_s[sb][0][wid][lane] = __builtin_bit_cast(bf16x8, make_uint4(ph[0], ph[1], ph[2], ph[3]));
+      pb_s[sb][1][wid][lane] = __builtin_bit_cast(bf16x8, make_uint4(pl[0], pl[1], pl[2], pl[3]));
     };
     prologue();
     if (ntiles > 0) {
@@ -498,7 +502,7 @@ __global__ __launch_bounds__(kMlaThreads, 1) void attn_mla_kernel(AttnPlan p) {
     // head blocks
     auto pv = [&](int buf, int sb) __attribute__((always_inline)) {
       const uint16_t* kt = ks_s[buf];
-      bf16x8 pbk[4];
+      bf16x8 pbk[4], pbl[4];
 #pragma unroll
       for (int hb = 0; hb < 4; ++hb) {
         const float alpha = alpha_s[sb][hb][n];
@@ -506,7 +510,8 @@ __global__ __launch_bounds__(kMlaThreads, 1) void attn_mla_kernel(AttnPlan p) {
 #pragma unroll
           for (int mc = 0; mc < 8; ++mc) o[hb][mc] *= alpha;
         }
-        pbk[hb] = pb_s[sb][hb][lane];
+        pbk[hb] = pb_s[sb][0][hb][lane];
+        pbl[hb] = pb_s[sb][1][hb][lane];
       }
       // A operand, m-tile mc: lane (g, n) needs column 128 cq + 16 mc + n of
       // the eight tokens of its k range; lane n of each group addresses
@@ -520,6 +525,9 @@ __global__ __launch_bounds__(kMlaThreads, 1) void attn_mla_kernel(AttnPlan p) {
 #pragma unroll
         for (int hb = 0; hb < 4; ++hb)
           o[hb][mc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pbk[hb], o[hb][mc], 0, 0, 0);
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb)
+          o[hb][mc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pbl[hb], o[hb][mc], 0, 0, 0);
         if ((mc & 3) == 3) __builtin_amdgcn_sched_barrier(0);  // bound the live V fragments
       }
     };
@@ -656,7 +664,6 @@ __global__ __launch_bounds__(64 * kGqaWaves) void attn_gqa_kernel(AttnPlan p) {
   };
 
   const float qk_scale = A.sm_scale * kLog2e;
-  const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3F803F80u);
   float m_run = -__builtin_huge_valf();  // base-2 reference max of head n
   float l_run = 0.f;
   f32x4 o[8];  // O^T: o[mc][i] = column 16 mc + 4 g + i of head n
@@ -702,20 +709,24 @@ __global__ __launch_bounds__(64 * kGqaWaves) void attn_gqa_kernel(AttnPlan p) {
     }
     const bool none = (m_run == -__builtin_huge_valf());
     float psum = 0.f;
-    uint32_t pk[4];
+    uint32_t ph[4], pl[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const float p0 = none ? 0.f : __builtin_amdgcn_exp2f(sv[2 * e] - m_run);
       const float p1 = none ? 0.f : __builtin_amdgcn_exp2f(sv[2 * e + 1] - m_run);
-      const bf16x2 pp = bf16x2{(__bf16)p0, (__bf16)p1};
-      psum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, psum, false);
-      pk[e] = __builtin_bit_cast(uint32_t, pp);
+      psum += p0 + p1;
+      const bf16x2 hi = bf16x2{(__bf16)p0, (__bf16)p1};
+      const bf16x2 lo = bf16x2{(__bf16)(p0 - (float)hi[0]), (__bf16)(p1 - (float)hi[1])};
+      ph[e] = __builtin_bit_cast(uint32_t, hi);
+      pl[e] = __builtin_bit_cast(uint32_t, lo);
     }
     psum += xlane16(psum);
     psum += swap_halves(psum);
     l_run += psum;
-    // B operand of P V: k = 8g + e  <->  token (e < 4 ? 4g + e : 16 + 4g + e - 4)
-    const bf16x8 pb = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+    // B operands of P V, high part and residual (p = hi + lo to 2^-17):
+    // k = 8g + e  <->  token (e < 4 ? 4g + e : 16 + 4g + e - 4)
+    const bf16x8 pb = __builtin_bit_cast(bf16x8, make_uint4(ph[0], ph[1], ph[2], ph[3]));
+    const bf16x8 pbl = __builtin_bit_cast(bf16x8, make_uint4(pl[0], pl[1], pl[2], pl[3]));
     // A operand, m-tile mc: lane (g, n) needs column 16 mc + n of those
     // eight tokens; lane n of each group addresses token row n / 4 of the
     // four and columns 4 (n % 4) .. +3
@@ -726,6 +737,7 @@ __global__ __launch_bounds__(64 * kGqaWaves) void attn_gqa_kernel(AttnPlan p) {
       const s16x4 r1 = lds_read_tr16(vb + 16 * kGqaRowV + 16 * mc);
       const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7));
       o[mc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, o[mc], 0, 0, 0);
+      o[mc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pbl, o[mc], 0, 0, 0);
     }
   };
 
