@@ -81,27 +81,6 @@ __device__ __forceinline__ float swap_halves(float v) {
   return __uint_as_float(o);
 }
 
-// Reductions over each row of 16 lanes (DPP row rotates and quad perms; no
-// LDS round trip).  Every lane of the row receives the result.
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float row16_max(float x) {
-  x = fmaxf(x, dpp_f<0x128>(x));  // row_ror:8
-  x = fmaxf(x, dpp_f<0x124>(x));  // row_ror:4
-  x = fmaxf(x, dpp_f<0x4E>(x));   // quad_perm [2,3,0,1]
-  x = fmaxf(x, dpp_f<0xB1>(x));   // quad_perm [1,0,3,2]
-  return x;
-}
-__device__ __forceinline__ float row16_sum(float x) {
-  x += dpp_f<0x128>(x);
-  x += dpp_f<0x124>(x);
-  x += dpp_f<0x4E>(x);
-  x += dpp_f<0xB1>(x);
-  return x;
-}
-
 // Inclusive prefix sum over the 64 lanes of a wave, entirely in DPP: shifts
 // by 1, 2, 4 and 8 within each row of 16 lanes (lanes shifted past the row
 // start add 0), then the row totals carried by the row broadcasts of lane 15
