@@ -1,0 +1,109 @@
+"""GPU: whole decode steps at seeded random shapes of every score kind,
+against the oracle.
+
+Sixteen shapes are drawn once from a fixed seed around the small workloads:
+batch 1..4, context lengths that end mid-tile, valid lengths down to a
+single token, k from 1 up to more than a request's valid units, 32 or 64
+index heads, 64..256 latent attention heads, paged and contiguous latent
+rows, and Fathom bit budgets from 8 to the full 512.  Each step is checked
+as in the other parity tests: scores within tau, the selection equal
+outside the near-tie band, the standalone top-k bit-exact on the GPU's own
+scores, and attention within 2e-3 of the oracle's attention over the GPU's
+selection.
+"""
+import numpy as np
+import pytest
+import torch
+
+import indexer_top_sparse_amd as isa
+from indexer_top_sparse_amd.runner import StepRunner
+import synth
+from oracle import compare as C
+from oracle import oracle as O
+
+from helpers import arrays, oracle_step, valid_units
+
+pytestmark = pytest.mark.gpu
+
+
+def _shapes():
+    g = np.random.default_rng(20261203)
+    out = []
+    for i in range(4):
+        B = int(g.integers(1, 5))
+        n = int(g.integers(300, 7000))
+        seq = tuple(int(x) for x in g.integers(1, n + 1, size=B))
+        out.append(synth.get("lightning_small").with_(
+            name=f"rand_lightning_{i}", B=B, n=n, seq_lens=seq,
+            k=int(g.choice([1, 64, 300, 1024])), idx_heads=int(g.choice([32, 64])),
+            hq=int(g.choice([64, 128, 192, 256])), page=int(g.choice([0, 64])),
+            seed=3100 + i))
+    for i in range(4):
+        B = int(g.integers(1, 5))
+        n = int(g.integers(200, 6000))
+        seq = tuple(int(x) for x in g.integers(1, n + 1, size=B))
+        out.append(synth.get("block_sparse_small").with_(
+            name=f"rand_block_{i}", B=B, n=n, seq_lens=seq,
+            k=int(g.choice([1, 4, 16, 200])), seed=3200 + i))
+    for i in range(4):
+        B = int(g.integers(1, 5))
+        n = int(g.integers(100, 5000))
+        seq = tuple(int(x) for x in g.integers(1, n + 1, size=B))
+        out.append(synth.get("tiny_fp32_small").with_(
+            name=f"rand_dot_{i}", B=B, n=n, seq_lens=seq,
+            k=int(g.choice([1, 17, 256, 600])), seed=3300 + i))
+    for i in range(4):
+        B = int(g.integers(1, 3))
+        n = int(g.integers(500, 40000))
+        seq = tuple(int(x) for x in g.integers(1, n + 1, size=B))
+        out.append(synth.get("fathom_small").with_(
+            name=f"rand_fathom_{i}", B=B, n=n, seq_lens=seq,
+            k=int(g.choice([1, 100, 300, 2048])), budget=int(g.choice([8, 92, 300, 512])),
+            seed=3400 + i))
+    return out
+
+
+SHAPES = _shapes()
+
+
+@pytest.mark.parametrize("w", SHAPES, ids=[w.name for w in SHAPES])
+def test_random_step_matches_oracle(w):
+    print(f"[random] {w.name} B={w.B} n={w.n} k={w.k} seq={w.seq_lens} hq={w.hq} "
+          f"page={w.page} budget={w.budget} idx_heads={w.idx_heads}", flush=True)
+    inp = synth.make_inputs(w, "cuda")
+    arr = arrays(inp)
+    ref = oracle_step(w, arr)
+    r = StepRunner(inp)
+    r.run()
+    torch.cuda.synchronize()
+    g = r.topk.cpu().numpy()
+    s = r.index_scores().clone()
+    torch.cuda.synchronize()
+    sn = s.cpu().numpy()
+    for b in range(w.B):
+        v = valid_units(w, b)
+        for h in range(g.shape[1]):
+            ok, err, tau = C.scores_ok(sn[b, h], ref["scores"][b, h], w.k, v)
+            assert ok, (b, h, "scores", err, tau)
+            ok, why = C.selection_ok(g[b, h], ref["sel"][b, h], ref["scores"][b, h], w.k, v)
+            assert ok, (b, h, why)
+    # the standalone top-k, bit-exact on the GPU's own scores
+    rows = s.shape[0] * s.shape[1]
+    flat = s.view(rows, -1)
+    vu = None
+    if inp.get("seq_lens") is not None:
+        vu = ((inp["seq_lens"] + w.block - 1) // w.block).to(torch.int32)
+    idx = torch.empty((rows, w.k), dtype=torch.int32, device="cuda")
+    ws = isa.workspace(isa.sparse_topk_workspace_size(rows, flat.shape[1], w.k))
+    isa.sparse_topk(flat, w.k, idx, None, vu, s.shape[1], ws)
+    torch.cuda.synchronize()
+    sc = flat.cpu().numpy().astype(np.float64)
+    gi = idx.cpu().numpy()
+    for row in range(rows):
+        exp = O.topk(sc[row], w.k, valid_units(w, row // s.shape[1]))
+        assert np.array_equal(gi[row], exp), ("topk", row)
+    # attention over the GPU's own selection
+    ref_g = oracle_step(w, arr, sel_in=g.astype(np.int64))
+    outs = ref_g["layers"][0]["out"] if w.kind == "block" else ref_g["out"]
+    ok, err = C.attn_ok(r.outs[0].cpu().numpy(), outs)
+    assert ok, ("attention", err)
