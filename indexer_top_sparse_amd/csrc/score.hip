@@ -615,20 +615,21 @@ hipError_t launch_read_depth(const sparse_index_args* a, int8_t* depth, int32_t*
 // ========================================================================
 // Fathom plane-prefix scan.  A thread owns one 32-bit word column of a
 // (request, KV head): 32 consecutive tokens.  The read planes (c, j) from
-// the list read_depth_kernel wrote are taken four at a time: the workgroup
-// first tabulates, for every group of four planes, the 16 sums of their
+// the list read_depth_kernel wrote are taken eight at a time: the workgroup
+// first tabulates, for every group of eight planes, the 256 sums of their
 // weights W_{c,j} over each subset of the group.  Per group a thread loads
-// the four plane words (coalesced across the workgroup), bit-slices them
-// into 4-bit indices -- nibble i of word q holds bit 8q + i of the four
-// planes, spread by three shift-or-mask steps per byte -- and adds the
-// table entry of each token's index: one extract, one LDS read and one add
-// per token and group instead of per token and plane.  The next four
-// groups are in flight while four are processed.
+// the eight plane words (coalesced across the workgroup) and transposes the
+// 8 x 8 bit blocks inside them (three rounds of masked swaps across word
+// pairs), after which byte q of word k is the 8-bit plane index of token
+// 8q + k.  Each token then adds one table entry: two ALU ops to form the
+// LDS address, one LDS read and one add per token and group, instead of an
+// add per token and plane.  The next two groups are in flight while two are
+// processed.
 // ========================================================================
 constexpr int kBpThreads = 1024;
 constexpr int kBpPassTok = kBpThreads * 32;             // 32768 tokens per workgroup pass
 constexpr int kBpMaxPasses = kHistPartMax / kBpPassTok;  // per workgroup (histogram part)
-static_assert(kPlaneBatch % 8 == 0, "padded plane list: whole pairs of four-plane groups");
+static_assert(kPlaneBatch % 8 == 0, "padded plane list: whole eight-plane groups");
 
 int bitplane_parts(const sparse_index_args& a) {
   const int passes = (a.n + kBpPassTok - 1) / kBpPassTok;
@@ -641,12 +642,28 @@ int bitplane_parts(const sparse_index_args& a) {
   return std::max(parts, 1);
 }
 
-// bit i of byte x -> bit 4i
-__device__ __forceinline__ uint32_t spread_nibbles(uint32_t x) {
-  x = (x | (x << 12)) & 0x000F000Fu;
-  x = (x | (x << 6)) & 0x03030303u;
-  x = (x | (x << 3)) & 0x11111111u;
-  return x;
+// In place: word k of eight, seen as four 8 x 8 bit matrices (byte q of
+// the eight words), is replaced by column k of each matrix, i.e. afterwards
+// bit j of byte q of w[k] is the old bit 8q + k of w[j].
+__device__ __forceinline__ void transpose_bytes8(uint32_t (&w)[8]) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t t = ((w[k] >> 4) ^ w[k + 4]) & 0x0F0F0F0Fu;
+    w[k + 4] ^= t;
+    w[k] ^= t << 4;
+  }
+#pragma unroll
+  for (int k = 0; k < 8; k += (k & 1) ? 3 : 1) {  // 0, 1, 4, 5
+    const uint32_t t = ((w[k] >> 2) ^ w[k + 2]) & 0x33333333u;
+    w[k + 2] ^= t;
+    w[k] ^= t << 2;
+  }
+#pragma unroll
+  for (int k = 0; k < 8; k += 2) {
+    const uint32_t t = ((w[k] >> 1) ^ w[k + 1]) & 0x55555555u;
+    w[k + 1] ^= t;
+    w[k] ^= t << 1;
+  }
 }
 
 __global__ __launch_bounds__(kBpThreads) void score_bitplane_kernel(
@@ -655,7 +672,8 @@ __global__ __launch_bounds__(kBpThreads) void score_bitplane_kernel(
   __shared__ uint32_t hist_s[kHistBins];
   __shared__ int32_t pl_s[512];
   __shared__ float pw_s[512];
-  __shared__ float lut_s[512 / 4 * 16];  // [group][subset of its four planes]
+  __shared__ float lut_s[512 / 8 * 256];  // [group][subset of its eight planes]
+  __shared__ __attribute__((aligned(16))) float stage_s[kBpThreads / 64][1024];  // per wave
   LdsHist lh{hist_s};
   const int h = blockIdx.y;
   const int b = blockIdx.z;
@@ -675,12 +693,12 @@ __global__ __launch_bounds__(kBpThreads) void score_bitplane_kernel(
   if (hist) lh.clear(kBpThreads);  // (ends with a barrier)
   else __syncthreads();
   // subset sums of each group, in plane order
-  for (int e = threadIdx.x; e < npad / 4 * 16; e += kBpThreads) {
-    const int g = e >> 4, m = e & 15;
+  for (int e = threadIdx.x; e < npad / 8 * 256; e += kBpThreads) {
+    const int g = e >> 8, m = e & 255;
     float x = 0.f;
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-      if ((m >> k) & 1) x += pw_s[4 * g + k];
+    for (int k = 0; k < 8; ++k)
+      if ((m >> k) & 1) x += pw_s[8 * g + k];
     lut_s[e] = x;
   }
   __syncthreads();
@@ -694,53 +712,69 @@ __global__ __launch_bounds__(kBpThreads) void score_bitplane_kernel(
     float acc[32];
 #pragma unroll
     for (int i = 0; i < 32; ++i) acc[i] = c0;
-    auto load_group = [&](uint32_t (&wd)[4], int p0) __attribute__((always_inline)) {
+    auto load_group = [&](uint32_t (&wd)[8], int p0) __attribute__((always_inline)) {
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
+      for (int k = 0; k < 8; ++k)
         wd[k] = __builtin_nontemporal_load(planes + (int64_t)pl_s[p0 + k] * nw + wc);
     };
-    auto add_group = [&](const uint32_t (&wd)[4], int p0) __attribute__((always_inline)) {
-      const float* lut = lut_s + (p0 >> 2) * 16;
+    auto add_group = [&](uint32_t (&wd)[8], int p0) __attribute__((always_inline)) {
+      transpose_bytes8(wd);
+      const float* lut = lut_s + (p0 >> 3) * 256;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        uint32_t nb = spread_nibbles(__builtin_amdgcn_ubfe(wd[0], 8 * q, 8));
+      for (int q = 0; q < 4; ++q)
 #pragma unroll
-        for (int k = 1; k < 4; ++k)
-          nb |= spread_nibbles(__builtin_amdgcn_ubfe(wd[k], 8 * q, 8)) << k;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[8 * q + i] += lut[__builtin_amdgcn_ubfe(nb, 4 * i, 4)];
-      }
+        for (int k = 0; k < 8; ++k) acc[8 * q + k] += lut[(wd[k] >> (8 * q)) & 0xFFu];
     };
-    // four groups per step, the next four in flight (npad is a multiple of
-    // 8, so the last step may hold only two)
-    constexpr int QG = 4;
-    uint32_t cur[QG][4];
+    // two groups per step, the next two in flight (npad is a multiple of 8,
+    // so the last step may hold only one)
+    constexpr int QG = 2;
+    uint32_t cur[QG][8];
 #pragma unroll
     for (int gq = 0; gq < QG; ++gq)
-      if (4 * gq < npad) load_group(cur[gq], 4 * gq);
-    for (int p0 = 0; p0 < npad; p0 += 4 * QG) {
-      uint32_t nxt[QG][4];
+      if (8 * gq < npad) load_group(cur[gq], 8 * gq);
+    for (int p0 = 0; p0 < npad; p0 += 8 * QG) {
+      uint32_t nxt[QG][8];
 #pragma unroll
       for (int gq = 0; gq < QG; ++gq)
-        if (p0 + 4 * QG + 4 * gq < npad) load_group(nxt[gq], p0 + 4 * QG + 4 * gq);
+        if (p0 + 8 * QG + 8 * gq < npad) load_group(nxt[gq], p0 + 8 * QG + 8 * gq);
 #pragma unroll
       for (int gq = 0; gq < QG; ++gq)
-        if (p0 + 4 * gq < npad) add_group(cur[gq], p0 + 4 * gq);
+        if (p0 + 8 * gq < npad) add_group(cur[gq], p0 + 8 * gq);
 #pragma unroll
       for (int gq = 0; gq < QG; ++gq)
 #pragma unroll
-        for (int k = 0; k < 4; ++k) cur[gq][k] = nxt[gq][k];
+        for (int k = 0; k < 8; ++k) cur[gq][k] = nxt[gq][k];
     }
-    if (w < nw) {
+    // A lane holds 32 consecutive tokens, so stores straight from acc would
+    // touch 64 cache lines per instruction.  The wave's 2048 tokens pass
+    // through its LDS slot instead, 1024 at a time (the lanes of one half,
+    // rows of 32 tokens, 16-byte chunks XOR-swizzled by row), and leave as
+    // coalesced 256-byte stores.
+    float* st = stage_s[threadIdx.x >> 6];
+    const int lane = threadIdx.x & 63;
+    const int t_wave = 32 * (w - lane);  // first token of the wave
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        const int t = 32 * w + i;
-        const float sc = t < valid ? acc[i] : -__builtin_huge_valf();
+    for (int r = 0; r < 2; ++r) {
+      if ((lane >> 5) == r) {
+        const int row = lane & 31;
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+          *(f32x4*)(st + 32 * row + 4 * (c ^ (row & 7))) =
+              f32x4{acc[4 * c], acc[4 * c + 1], acc[4 * c + 2], acc[4 * c + 3]};
+      }
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int row = 2 * j + (lane >> 5), col = lane & 31;
+        const float v = st[32 * row + 4 * ((col >> 2) ^ (row & 7)) + (col & 3)];
+        const int t = t_wave + 1024 * r + 64 * j + lane;
+        const float sc = t < valid ? v : -__builtin_huge_valf();
         if (t < n) {
           srow[t] = sc;
           if (hist && t < valid) lh.add(sc);
         }
       }
+      __builtin_amdgcn_wave_barrier();
     }
   }
   if (hist) {
