@@ -255,6 +255,7 @@ sd::TopkPlan make_topk_plan(const IndexLayout& L, char* ws, const float* scores,
   // spans that cover the row
   p.fused = part_span > 0 && hist_parts >= 1 && hist_parts <= sd::kFuseMaxParts &&
             (int64_t)hist_parts * part_span >= L.n_units;
+  p.direct = L.n_units <= sd::kTopkDirectMax;
   p.bstar = (uint32_t*)(ws + L.bstar);
   p.cand_total = (uint32_t*)(ws + L.cand_total);
   p.cand_key = (uint32_t*)(ws + L.cand_key);
@@ -272,12 +273,14 @@ int run_topk(const sd::TopkPlan& p, bool hist_ready, hipStream_t s) {
     HIPCHECK(sd::launch_topk_select(p, s));
     return SPARSE_OK;
   }
-  if (!hist_ready) HIPCHECK(sd::launch_topk_hist(p, s));
-  if (p.fused) {
-    HIPCHECK(sd::launch_topk_filter_fused(p, s));
-  } else {
-    HIPCHECK(sd::launch_topk_bin(p, s));
-    HIPCHECK(sd::launch_topk_filter(p, s));
+  if (!p.direct) {
+    if (!hist_ready) HIPCHECK(sd::launch_topk_hist(p, s));
+    if (p.fused) {
+      HIPCHECK(sd::launch_topk_filter_fused(p, s));
+    } else {
+      HIPCHECK(sd::launch_topk_bin(p, s));
+      HIPCHECK(sd::launch_topk_filter(p, s));
+    }
   }
   HIPCHECK(sd::launch_topk_select(p, s));
   return SPARSE_OK;
@@ -486,7 +489,7 @@ int sparse_decode_step(const sparse_index_args* ia, const sparse_attn_args* aa, 
                                    unit, k, topk_out, nullptr, L.hist_parts,
                                    sd::score_part_span(*ia));
   if (ia->n > 0) {
-    rc = run_scores(*ia, L, w, scores, tp.hist, s);
+    rc = run_scores(*ia, L, w, scores, tp.direct ? nullptr : tp.hist, s);
     if (rc) return rc;
   }
   rc = run_topk(tp, true, s);

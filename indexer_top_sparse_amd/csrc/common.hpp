@@ -35,6 +35,9 @@ constexpr int kHistPartWords = kHistWords + kCoarseBins;
 // Rows whose parts are at most this many contiguous unit spans take the
 // fused filter (no separate bin kernel).
 constexpr int kFuseMaxParts = 64;
+// Rows of at most this many units skip the histogram and filter kernels:
+// the select kernel stages the whole row in LDS and finds b* itself.
+constexpr int kTopkDirectMax = 12288;
 
 // Pointer into the global address space: loads through it compile to
 // global_load (vector memory counter only) rather than flat_load.
@@ -168,6 +171,7 @@ struct TopkPlan {
   int parts;         // histogram parts per row
   int part_span;     // units per part (part q: units [q span, (q + 1) span))
   int fused;         // candidates in one contiguous list per row (fused filter)
+  int direct;        // rows of <= kTopkDirectMax units: the select alone, on the scores
   uint32_t* bstar;   // [rows][2]: boundary bin b*, units in higher bins
   uint32_t* cand_total;  // [rows]: candidates of the row (fused filter)
   uint32_t* cand_key;  // [rows][n_units]

@@ -23,6 +23,9 @@
 //   filter  rows x chunks workgroups: compacts, in index order, every unit
 //           whose bin is >= b* into its chunk's slice of a candidate buffer
 //           (keys and indices) and stores the chunk count (one block scan).
+//   Rows of at most kTopkDirectMax units take the select alone: it stages
+//   the row's own keys as the candidates and counts their top 12 bits to
+//   find b* first.
 //   select  one workgroup per row: stages the candidates in LDS while
 //           counting bits [19:8] of those in bin b*, resolves
 //           the last 8 bits in a second LDS histogram, which gives the exact
@@ -418,6 +421,7 @@ hipError_t launch_topk_filter_fused(const TopkPlan& p, hipStream_t s) {
 // ------------------------------------------------------------------- select
 constexpr int kSelThreads = 1024;
 constexpr int kSelCap = 12288;  // candidates staged in LDS (96 KB)
+static_assert(kTopkDirectMax <= kSelCap, "a direct row fits in LDS");
 
 __device__ __forceinline__ int find_chunk(const int* excl, int nchunks, int p) {
   // largest c with excl[c] <= p
@@ -448,8 +452,8 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkPlan p) {
   }
   if (k_eff <= 0) return;
 
-  const uint32_t b1 = p.bstar[2 * r];
-  int above = (int)p.bstar[2 * r + 1];
+  uint32_t b1;
+  int above;
   const int wid = tid >> 6;
   const int lane = tid & 63;
 
@@ -463,7 +467,32 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkPlan p) {
   uint32_t skey[kSelSpec];
   int32_t sidx[kSelSpec];
   int M = 0;
-  if (p.fused) {
+  if (p.direct) {
+    // the row is the candidate list: every valid unit, in index order; its
+    // top 12 key bits give b* and the count above it
+    M = v;
+    const float* sr = p.scores + (int64_t)r * p.row_stride;
+    __syncthreads();  // hs cleared
+    for (int q = tid; q < M; q += kSelThreads) {
+      const uint32_t key = score_key(sr[q]);
+      ckey_s[q] = key;
+      cidx_s[q] = q;
+      atomicAdd(&hs[key >> 20], 1u);
+    }
+    if (tid == 0) { res[0] = 0; res[1] = 0; }
+    __syncthreads();
+    find_bin_from_top<kSelThreads>(hs, kHistBins, k_eff, scan_lds, res);
+    b1 = (uint32_t)res[0];
+    above = res[1];
+    for (int i = tid; i < kHistBins; i += kSelThreads) hs[i] = 0u;
+    __syncthreads();
+    for (int q = tid; q < M; q += kSelThreads) {
+      const uint32_t key = ckey_s[q];
+      if ((key >> 20) == b1) atomicAdd(&hs[(key >> 8) & 0xFFFu], 1u);
+    }
+  } else if (p.fused) {
+    b1 = p.bstar[2 * r];
+    above = (int)p.bstar[2 * r + 1];
     const uint32_t* ck0 = p.cand_key + (int64_t)r * p.n_units;
     const int32_t* ci0 = p.cand_idx + (int64_t)r * p.n_units;
 #pragma unroll
@@ -475,6 +504,8 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkPlan p) {
     M = min((int)p.cand_total[r], p.n_units);
     __syncthreads();
   } else {
+    b1 = p.bstar[2 * r];
+    above = (int)p.bstar[2 * r + 1];
     const uint32_t* cc = p.chunk_cnt + (int64_t)r * p.n_chunks;
     for (int base = 0; base < p.n_chunks; base += kSelThreads) {
       int c = base + tid;
@@ -497,8 +528,10 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkPlan p) {
   // stage the candidates (in index order) in LDS when they fit: the fused
   // filter's single list by all threads, per-chunk slices by wave w copying
   // chunks w, w + 16, ...
-  const bool inlds = M <= kSelCap;
-  if (inlds && p.fused) {
+  const bool inlds = p.direct || M <= kSelCap;
+  if (p.direct) {
+    // staged and counted above
+  } else if (inlds && p.fused) {
 #pragma unroll
     for (int j = 0; j < kSelSpec; ++j) {
       const int q = tid + j * kSelThreads;
