@@ -1,9 +1,11 @@
-"""GPU: the standalone top-k (sparse_topk) on both of its kernel paths.
+"""GPU: the standalone top-k (sparse_topk) on each of its kernel paths.
 
-Rows of up to 64 histogram parts (4096 units each, so n_units <= 262144)
-take the fused filter, which finds the boundary bin from the parts' coarse
-counts and writes one candidate list per row; longer rows take the
-bin / per-chunk filter kernels.  Each case here is checked element by
+Rows of at most 12288 units take the select kernel alone, which stages the
+whole row and finds the boundary bin itself.  Longer rows of up to 64
+histogram parts (4096 units each, so n_units <= 262144) take the fused
+filter, which finds the boundary bin from the parts' coarse counts and
+writes one candidate list per row; longer rows still take the bin /
+per-chunk filter kernels.  Each case here is checked element by
 element against the oracle's exact top-k (ties to the lower index, output
 ascending, -1 padding past the valid units), on score patterns chosen to
 stress the bin search and the per-part candidate offsets: heavy ties,
@@ -45,6 +47,11 @@ CASES = [
     ("special", 2, 70000, 777, [70000, 12345]),
     ("normal", 4, 4096, 1, None),
     ("normal", 3, 5001, 5001, [5001, 4000, 0]),      # k = n; an empty row
+    # rows of at most 12288 units take the select kernel alone
+    ("ties", 3, 12288, 700, [12288, 12287, 600]),    # the longest such row
+    ("ties", 2, 12289, 700, None),                   # one unit more: fused filter
+    ("special", 2, 3000, 64, [3000, 17]),
+    ("rising", 2, 1280, 32, None),
 ]
 
 
