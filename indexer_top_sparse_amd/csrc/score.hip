@@ -314,28 +314,9 @@ __global__ __launch_bounds__(kLtThreads) void score_lightning_kernel(
   const int col = lane & 31;
   const int n = a.n;
   const int valid = valid_len(a.seq_lens, b, n);
-  if (hist) lh.clear(kLtThreads);
 
-  // A operands: q[32*mt + col][64*half + 8*s + 0..7]
   bf16x8 qa[MT][8];
-  const uint16_t* qb = (const uint16_t*)a.q + (int64_t)b * a.q_stride_b;
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const uint16_t* qh = qb + (int64_t)(32 * mt + col) * a.q_stride_h + 64 * half;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) qa[mt][s] = *(const bf16x8*)(qh + 8 * s);
-  }
-  // weights of the heads this lane's accumulators hold
   float wv[MT][16];
-  const float* wb = a.head_w + (int64_t)b * a.w_stride_b;
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj)
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii)
-        wv[mt][4 * jj + ii] = wb[32 * mt + 8 * jj + 4 * half + ii];
-
   const uint8_t* kb = (const uint8_t*)a.keys + (int64_t)b * a.k_stride_b;
   const float* ksb = a.k_scale + (int64_t)b * a.ks_stride_b;
   float* srow = scores + (int64_t)b * n_units;
@@ -416,9 +397,33 @@ __global__ __launch_bounds__(kLtThreads) void score_lightning_kernel(
   // the guarded loop.
   static_assert(TPW % kLtStages == 0, "whole stage groups");
   LtTile buf[kLtStages];
-  if (ntiles == TPW && t0 + (TPW - 1) * kStride + 32 <= n) {
+  const bool full = ntiles == TPW && t0 + (TPW - 1) * kStride + 32 <= n;
+  // the first tiles' loads go out before q, the weights and the histogram
+  // clear, whose latency they then cover
+  if (full) {
 #pragma unroll
     for (int s = 0; s < kLtStages; ++s) issue(buf[s], s);
+  }
+  // A operands: q[32*mt + col][64*half + 8*s + 0..7]
+  const uint16_t* qb = (const uint16_t*)a.q + (int64_t)b * a.q_stride_b;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const uint16_t* qh = qb + (int64_t)(32 * mt + col) * a.q_stride_h + 64 * half;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qa[mt][s] = *(const bf16x8*)(qh + 8 * s);
+  }
+  // weights of the heads this lane's accumulators hold
+  const float* wb = a.head_w + (int64_t)b * a.w_stride_b;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii)
+        wv[mt][4 * jj + ii] = wb[32 * mt + 8 * jj + 4 * half + ii];
+
+  if (hist) lh.clear(kLtThreads);
+  if (full) {
     for (int g = 0; g < TPW / kLtStages - 1; ++g) {
 #pragma unroll
       for (int s = 0; s < kLtStages; ++s) {
