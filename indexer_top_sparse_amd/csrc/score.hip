@@ -158,25 +158,9 @@ __global__ __launch_bounds__(kDotThreads) void score_dot_kernel(
   const int n = a.n;
   const int valid = valid_len(a.seq_lens, b, n);
 
-  if (threadIdx.x < 128) {
-    double acc = 0.0;
-    for (int h = 0; h < a.n_heads; ++h) {
-      const T* qh = (const T*)a.q + (int64_t)b * a.q_stride_b + (int64_t)h * a.q_stride_h;
-      float x;
-      if constexpr (sizeof(T) == 4) x = qh[threadIdx.x];
-      else x = bf16_bits_to_f32(qh[threadIdx.x]);
-      acc += (double)x;
-    }
-    qbar_s[threadIdx.x] = (float)acc;
-  }
-  if (hist) lh.clear(kDotThreads);  // (ends with a barrier)
-  else __syncthreads();
-
   const int c = lane % LPR;  // the 16-byte column chunk this lane reads
   const int g = lane / LPR;  // row within a load instruction
   float qv[PL];
-#pragma unroll
-  for (int e = 0; e < PL; ++e) qv[e] = qbar_s[c * PL + e];
 
   const char* kb = (const char*)a.keys + (int64_t)b * a.k_stride_b * (int64_t)sizeof(T);
   const int64_t rstride = a.k_stride_t * (int64_t)sizeof(T);
@@ -226,9 +210,29 @@ __global__ __launch_bounds__(kDotThreads) void score_dot_kernel(
     }
   };
 
+  // the first tiles' loads go out before q_bar is formed and the histogram
+  // cleared, whose latency they then cover
   Tile buf[NS];
 #pragma unroll
   for (int st = 0; st < NS; ++st) issue(buf[st], st);
+
+  if (threadIdx.x < 128) {
+    double acc = 0.0;
+#pragma unroll 8
+    for (int h = 0; h < a.n_heads; ++h) {
+      const T* qh = (const T*)a.q + (int64_t)b * a.q_stride_b + (int64_t)h * a.q_stride_h;
+      float x;
+      if constexpr (sizeof(T) == 4) x = qh[threadIdx.x];
+      else x = bf16_bits_to_f32(qh[threadIdx.x]);
+      acc += (double)x;
+    }
+    qbar_s[threadIdx.x] = (float)acc;
+  }
+  if (hist) lh.clear(kDotThreads);  // (ends with a barrier)
+  else __syncthreads();
+#pragma unroll
+  for (int e = 0; e < PL; ++e) qv[e] = qbar_s[c * PL + e];
+
   for (int r = 0; r < rounds; r += NS) {
 #pragma unroll
     for (int st = 0; st < NS; ++st) {
