@@ -278,6 +278,35 @@ int sparse_append_token(const sparse_index_args* ia, const sparse_attn_args* aa,
                         const int32_t* pos, const float* index_key_new,
                         const void* k_new, const void* v_new, void* stream);
 
+/* Hot-buffer replacement, to run right after the step that used the hot
+ * buffer ([XM] Figure 1 and decode-path list: the hot KV buffer in HBM and
+ * the fetch of the missing selected rows; the page keeps HiSparse's cache
+ * management without stating its rule, and this is least recently used).
+ * Call it with the same ia (NULL after sparse_gather_attn_decode), aa, k,
+ * sel_unit and workspace as that call, whose fetched rows the workspace
+ * still holds, and with hot_slot unchanged since.  Per request:
+ *   - a selected token held in a slot (a hit) stamps the slot with step;
+ *   - the selected tokens not held (misses), in selection order, take the
+ *     slots not stamped step that have the smallest (stamp, slot index),
+ *     in ascending slot order: the slot's previous token loses its slot
+ *     (hot_slot -1), the miss's row is copied into hot_kv, hot_slot of the
+ *     miss becomes the slot, and the slot is stamped step;
+ *   - misses beyond the slots available stay out.
+ * sel: [B][k] the step's selection (distinct tokens, -1 padding); n_slots:
+ * the hot_kv rows per request (1..8192); at most 4096 selected tokens per
+ * request.  slot_token [B][n_slots] int32: the token a slot holds, or -1;
+ * slot_stamp [B][n_slots] int32: the step of the slot's last hit or fill,
+ * -1 for never (stamps >= -1; a stamp >= step marks a slot as kept this
+ * time).  step >= 0 must grow from call to call for the order to be least
+ * recently used.  hot_slot (aa) and hot_kv (aa) are written in place; it
+ * is the caller's job to keep hot_slot and slot_token consistent (each the
+ * other's inverse) between calls.  Prefetch is not done. */
+int sparse_hot_update(const sparse_index_args* ia, const sparse_attn_args* aa,
+                      const int32_t* sel, int32_t k, int32_t sel_unit,
+                      int32_t n_slots, int32_t step, int32_t* slot_token,
+                      int32_t* slot_stamp, void* ws, size_t ws_bytes,
+                      void* stream);
+
 /* Device-visible address of pinned host memory allocated with
  * hipHostMalloc (e.g. a pinned torch tensor); used for host_kv. */
 int sparse_host_device_pointer(void* host_ptr, void** dev_ptr);

@@ -92,10 +92,12 @@ def lib() -> ctypes.CDLL:
                                          _vp, _vp, ctypes.c_size_t, _vp]
         L.sparse_host_device_pointer.argtypes = [_vp, P(_vp)]
         L.sparse_append_token.argtypes = [P(IndexArgs), P(AttnArgs), _vp, _vp, _vp, _vp, _vp]
+        L.sparse_hot_update.argtypes = [P(IndexArgs), P(AttnArgs), _vp, _i32, _i32, _i32,
+                                        _i32, _vp, _vp, _vp, ctypes.c_size_t, _vp]
         for f in ("sparse_workspace_size", "sparse_topk_workspace_size",
                   "sparse_read_depth", "sparse_index_score", "sparse_topk",
                   "sparse_gather_attn_decode", "sparse_decode_step",
-                  "sparse_host_device_pointer", "sparse_append_token"):
+                  "sparse_host_device_pointer", "sparse_append_token", "sparse_hot_update"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -335,6 +337,21 @@ def sparse_append_token(ia: _Holder | None, aa: _Holder | None, pos: torch.Tenso
                                      aa.ref() if aa is not None else None,
                                      _p(pos), _p(index_key_new), _p(k_new), _p(v_new),
                                      _stream(stream)))
+
+
+def sparse_hot_update(ia: _Holder | None, aa: _Holder, sel: torch.Tensor, k: int,
+                      sel_unit: int, n_slots: int, step: int, slot_token: torch.Tensor,
+                      slot_stamp: torch.Tensor, ws: torch.Tensor, stream=None) -> None:
+    """Least-recently-used replacement in the hot buffer of `aa` after the
+    step (sparse_decode_step with `ia`, or sparse_gather_attn_decode with
+    ia None) that selected `sel` and staged its misses in `ws`.  slot_token
+    and slot_stamp: [B][n_slots] int32, updated with aa's hot_slot / hot_kv."""
+    for t in (sel, slot_token, slot_stamp):
+        if not t.is_contiguous() or t.dtype != torch.int32:
+            raise ValueError("sel / slot_token / slot_stamp must be contiguous int32")
+    _check(lib().sparse_hot_update(ia.ref() if ia is not None else None, aa.ref(), _p(sel),
+                                   k, sel_unit, n_slots, step, _p(slot_token),
+                                   _p(slot_stamp), _p(ws), ws.numel(), _stream(stream)))
 
 
 def host_device_pointer(host: torch.Tensor) -> int:

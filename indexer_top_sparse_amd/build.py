@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsparse_decode.so")
-SOURCES = ["api.hip", "score.hip", "topk.hip", "attn.hip", "append.hip"]
+SOURCES = ["api.hip", "score.hip", "topk.hip", "attn.hip", "append.hip", "hot.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -562,6 +562,48 @@ int sparse_append_token(const sparse_index_args* ia, const sparse_attn_args* aa,
   return SPARSE_OK;
 }
 
+int sparse_hot_update(const sparse_index_args* ia, const sparse_attn_args* aa,
+                      const int32_t* sel, int32_t k, int32_t sel_unit, int32_t n_slots,
+                      int32_t step, int32_t* slot_token, int32_t* slot_stamp, void* ws,
+                      size_t ws_bytes, void* stream) {
+  int rc = check_attn(aa, 1, k, sel_unit);
+  if (rc) return rc;
+  CHECK(aa->hot_slot, SPARSE_EINVAL, "hot_slot NULL: no hot buffer to update");
+  CHECK(n_slots >= 1 && n_slots <= sd::kHotMaxSlots, SPARSE_EUNSUPPORTED,
+        "n_slots %d outside 1..%d", n_slots, sd::kHotMaxSlots);
+  CHECK(step >= 0, SPARSE_EINVAL, "step %d < 0", step);
+  CHECK((int64_t)k * sel_unit <= sd::kHotMaxSel, SPARSE_EUNSUPPORTED,
+        "%d selected tokens above %d", k * sel_unit, sd::kHotMaxSel);
+  size_t base = 0;
+  if (ia) {
+    rc = check_index(ia);
+    if (rc) return rc;
+    const int unit = ia->kind == SPARSE_SCORE_DOT ? ia->block_size : 1;
+    CHECK(unit == sel_unit, SPARSE_EINVAL, "sel_unit %d differs from the index unit %d",
+          sel_unit, unit);
+    CHECK(ia->batch == aa->batch, SPARSE_EINVAL, "index batch %d != attention batch %d",
+          ia->batch, aa->batch);
+    base = index_layout(*ia, true).end;
+  }
+  if (aa->batch == 0) return SPARSE_OK;
+  CHECK(sel && slot_token && slot_stamp, SPARSE_EINVAL, "sel / slot_token / slot_stamp NULL");
+  AttnLayout L = attn_layout(*aa, k * sel_unit, base);
+  CHECK(ws && ws_bytes >= L.end, SPARSE_EWORKSPACE, "workspace %zu < %zu", ws_bytes, L.end);
+  sd::HotPlan p;
+  p.a = *aa;
+  p.sel = sel;
+  p.k = k;
+  p.sel_unit = sel_unit;
+  p.k_tokens = k * sel_unit;
+  p.n_slots = n_slots;
+  p.step = step;
+  p.slot_token = slot_token;
+  p.slot_stamp = slot_stamp;
+  p.staging = (const uint16_t*)((const char*)ws + L.staging);
+  HIPCHECK(sd::launch_hot_update(p, (hipStream_t)stream));
+  return SPARSE_OK;
+}
+
 int sparse_host_device_pointer(void* host_ptr, void** dev_ptr) {
   CHECK(host_ptr && dev_ptr, SPARSE_EINVAL, "NULL pointer");
   HIPCHECK(hipHostGetDevicePointer(dev_ptr, host_ptr, 0));

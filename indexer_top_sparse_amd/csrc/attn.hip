@@ -51,11 +51,6 @@ struct RowAddr {
   }
 };
 
-__device__ __forceinline__ int valid_tokens(const sparse_attn_args& a, int b) {
-  if (!a.seq_lens) return a.n;
-  int v = a.seq_lens[b];
-  return v < 0 ? 0 : (v > a.n ? a.n : v);
-}
 
 // One halving step of a reduce-scatter over N partials: partner lanes
 // (given by xch) exchange halves; a lane with `up` keeps the upper half.
@@ -69,14 +64,6 @@ __device__ __forceinline__ void rs_halve(float* p, bool up, F xch) {
   }
 }
 
-// Token of selection list position j (-1 if padding or past seq_len).
-__device__ __forceinline__ int sel_token(const int32_t* selrow, int j, int unit,
-                                         int valid) {
-  int u = selrow[j / unit];
-  if (u < 0) return -1;
-  int t = u * unit + (j % unit);
-  return t < valid ? t : -1;
-}
 
 // =================================================================== fp32
 // One workgroup per (request, KV head, group of up to 8 query heads, split);

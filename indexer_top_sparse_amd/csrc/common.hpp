@@ -130,6 +130,23 @@ __device__ __forceinline__ uint32_t lane_xor_u32(uint32_t v, int m) {
   }
 }
 
+// ------------------------------------------------------ selection helpers
+// Valid tokens of request b of the attention arguments.
+__device__ __forceinline__ int valid_tokens(const sparse_attn_args& a, int b) {
+  if (!a.seq_lens) return a.n;
+  int v = a.seq_lens[b];
+  return v < 0 ? 0 : (v > a.n ? a.n : v);
+}
+
+// Token of selection list position j (-1 if padding or past seq_len).
+__device__ __forceinline__ int sel_token(const int32_t* selrow, int j, int unit,
+                                         int valid) {
+  int u = selrow[j / unit];
+  if (u < 0) return -1;
+  int t = u * unit + (j % unit);
+  return t < valid ? t : -1;
+}
+
 // ---------------------------------------------------------------- block scan
 // Inclusive prefix sum over a block of NT threads (NT multiple of 64).
 // `lds` must hold NT/64 + 1 ints.  Returns the inclusive sum for the thread
@@ -226,6 +243,19 @@ hipError_t launch_attn_f32(const AttnPlan& p, hipStream_t s);
 hipError_t launch_attn_bf16(const AttnPlan& p, hipStream_t s);
 hipError_t launch_attn_combine(const AttnPlan& p, hipStream_t s);
 hipError_t launch_miss_fetch(const AttnPlan& p, hipStream_t s);
+// Hot-buffer replacement after a step (hot.hip).
+constexpr int kHotMaxSlots = 8192;  // slots per request
+constexpr int kHotMaxSel = 4096;    // selected tokens per request
+struct HotPlan {
+  sparse_attn_args a;          // hot_slot and hot_kv are written
+  const int32_t* sel;          // [B][k] the step's selection
+  int k, sel_unit, k_tokens;
+  int n_slots, step;
+  int32_t* slot_token;         // [B][n_slots] token held, or -1
+  int32_t* slot_stamp;         // [B][n_slots] step of the last use
+  const uint16_t* staging;     // [B][k_tokens][d_qk] the step's fetched rows
+};
+hipError_t launch_hot_update(const HotPlan& p, hipStream_t s);
 hipError_t launch_append(const sparse_index_args* ia, const sparse_attn_args* aa,
                          const int32_t* pos, const float* key_new, const void* k_new,
                          const void* v_new, int batch, hipStream_t s);

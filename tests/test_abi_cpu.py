@@ -198,3 +198,40 @@ def test_append_validation_codes():
     a = _lightning(B=0)
     assert L.sparse_append_token(ctypes.byref(a), None, None, None, None, None, None) == \
         isa.SPARSE_OK
+
+
+def _hot_attn(B=2, n=1000):
+    a = _mla_attn(B, n)
+    a.k_cache, a.page_table, a.pt_stride_b, a.page_size = None, None, 0, 0
+    a.hot_slot, a.hs_stride_b = FAKE, n
+    a.hot_kv, a.hot_stride_b, a.hot_stride_s = FAKE, 64 * 576, 576
+    a.host_kv, a.host_stride_b, a.host_stride_t = FAKE, n * 576, 576
+    return a
+
+
+def test_hot_update_validation_codes():
+    L = isa.lib()
+    big = 1 << 30
+    a = _hot_attn()
+    ok = (FAKE, 16, 1, 64, 3, FAKE, FAKE, FAKE, big, None)
+    # no hot buffer in the arguments
+    assert L.sparse_hot_update(None, ctypes.byref(_mla_attn()), *ok) == isa.SPARSE_EINVAL
+    # slot count, step and selection size limits
+    assert L.sparse_hot_update(None, ctypes.byref(a), FAKE, 16, 1, 0, 3, FAKE, FAKE, FAKE,
+                               big, None) == isa.SPARSE_EUNSUPPORTED
+    assert L.sparse_hot_update(None, ctypes.byref(a), FAKE, 16, 1, 8193, 3, FAKE, FAKE, FAKE,
+                               big, None) == isa.SPARSE_EUNSUPPORTED
+    assert L.sparse_hot_update(None, ctypes.byref(a), FAKE, 16, 1, 64, -1, FAKE, FAKE, FAKE,
+                               big, None) == isa.SPARSE_EINVAL
+    assert L.sparse_hot_update(None, ctypes.byref(a), FAKE, 4097, 1, 64, 3, FAKE, FAKE, FAKE,
+                               big, None) == isa.SPARSE_EUNSUPPORTED
+    # NULL state, too small a workspace, a unit that differs from the index's
+    assert L.sparse_hot_update(None, ctypes.byref(a), FAKE, 16, 1, 64, 3, None, FAKE, FAKE,
+                               big, None) == isa.SPARSE_EINVAL
+    assert L.sparse_hot_update(None, ctypes.byref(a), FAKE, 16, 1, 64, 3, FAKE, FAKE, FAKE,
+                               16, None) == isa.SPARSE_EWORKSPACE
+    ia = _lightning()
+    assert L.sparse_hot_update(ctypes.byref(ia), ctypes.byref(a), FAKE, 16, 64, 64, 3, FAKE,
+                               FAKE, FAKE, big, None) == isa.SPARSE_EINVAL
+    # an empty batch is a no-op
+    assert L.sparse_hot_update(None, ctypes.byref(_hot_attn(B=0)), *ok) == isa.SPARSE_OK

@@ -1,0 +1,155 @@
+"""GPU: least-recently-used hot-buffer replacement (sparse_hot_update) after
+a step, against the oracle (oracle/hot.py), bit for bit.
+
+* Attention-only steps (sparse_gather_attn_decode, which fetches the missed
+  rows into the workspace) on a random hot-buffer state -- resident tokens,
+  empty slots, stamps from -1 up -- then a sequence of updates with
+  overlapping selections, padding entries and ragged valid lengths, at
+  several buffer sizes, including buffers smaller than a selection (misses
+  that stay out) and ties of stamps.  After every update the token -> slot
+  map, the slot -> token map, the stamps and every hot row are compared with
+  the oracle's.
+* The fused step (sparse_decode_step, lightning indexer) on the small
+  hot-buffer workload, then the update with the step's own selection.
+"""
+import numpy as np
+import pytest
+import torch
+
+import indexer_top_sparse_amd as isa
+import synth
+from synth.gen import build_hot_buffer
+from indexer_top_sparse_amd.runner import StepRunner
+from oracle.hot import hot_update
+
+pytestmark = pytest.mark.gpu
+
+
+def _bits(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def _oracle_all(hs, st, ss, hk, host, sel, valid, step):
+    out = [np.empty_like(x) for x in (hs, st, ss, hk)]
+    for b in range(hs.shape[0]):
+        r = hot_update(hs[b], st[b], ss[b], hk[b], host[b], sel[b], valid[b], step)
+        for o, x in zip(out, r):
+            o[b] = x
+    return out
+
+
+def _check(state, ref, where):
+    hs, st, ss, hk = state
+    names = ("hot_slot", "slot_token", "slot_stamp", "hot_kv")
+    got = (hs.cpu().numpy(), st.cpu().numpy(), ss.cpu().numpy(), _bits(hk))
+    for name, g, r in zip(names, got, ref):
+        bad = np.argwhere(g != r)
+        assert bad.size == 0, (where, name, bad[:5].tolist())
+
+
+CASES = [
+    # (B, n, slots, k, steps, valid lengths)
+    (3, 3000, 1024, 512, 4, [3000, 2500, 700]),
+    (2, 5000, 300, 256, 3, None),       # a buffer a little larger than a selection
+    (2, 2000, 64, 100, 5, [2000, 90]),  # fewer slots than selected: misses stay out
+]
+
+
+@pytest.mark.parametrize("B,n,S,k,steps,valid", CASES,
+                         ids=[f"S{c[2]}-k{c[3]}" for c in CASES])
+def test_hot_update_sequence_matches_oracle(B, n, S, k, steps, valid):
+    print(f"[hot-update] B={B} n={n} slots={S} k={k} steps={steps}", flush=True)
+    g = np.random.default_rng(S + k + n)
+    Hq, d = 64, 576
+    vl = np.array(valid if valid is not None else [n] * B)
+    host_f = g.normal(size=(B, n, d)).astype(np.float32)
+    host = torch.from_numpy(host_f).to(torch.bfloat16).pin_memory()
+    host_bits = host.view(torch.int16).numpy().view(np.uint16)
+    # a random starting state: some resident tokens, some empty slots
+    hs = np.full((B, n), -1, np.int32)
+    st = np.full((B, S), -1, np.int32)
+    ss = np.full((B, S), -1, np.int32)
+    hk = np.zeros((B, S, d), np.uint16)
+    for b in range(B):
+        m = int(g.integers(0, min(S, vl[b]) + 1))
+        toks = g.choice(vl[b], size=m, replace=False)
+        slots = g.choice(S, size=m, replace=False)
+        for t, s in zip(toks, slots):
+            hs[b, t], st[b, s], ss[b, s] = s, t, int(g.integers(-1, 4))
+            hk[b, s] = host_bits[b, t]
+    dev = "cuda"
+    hot_slot = torch.from_numpy(hs).to(dev)
+    slot_token = torch.from_numpy(st).to(dev)
+    slot_stamp = torch.from_numpy(ss).to(dev)
+    hot_kv = torch.from_numpy(hk.view(np.int16)).to(dev).view(torch.bfloat16)
+    q = torch.from_numpy(g.normal(size=(B, Hq, d)).astype(np.float32) * 0.1).to(torch.bfloat16).to(dev)
+    seq = torch.from_numpy(vl.astype(np.int32)).to(dev)
+    aa = isa.attn_args(q, None, n=n, seq_lens=seq, sm_scale=d ** -0.5,
+                       hot_slot=hot_slot, hot_kv=hot_kv, host_kv=host)
+    ws = isa.workspace(isa.sparse_workspace_size(None, aa, k))
+    out = torch.empty((B, Hq, 512), dtype=torch.float32, device=dev)
+    prev = [np.array([], dtype=np.int64) for _ in range(B)]
+    state = [hs, st, ss, hk]
+    for i in range(steps):
+        step = 10 + i
+        sel = np.full((B, k), -1, np.int32)
+        for b in range(B):
+            # half of the last selection again, the rest new
+            keep = prev[b][: prev[b].size // 2]
+            fresh = g.choice(n, size=k, replace=False)
+            pick = np.unique(np.concatenate([keep, fresh]))[:k]
+            pick = np.sort(g.permutation(pick)[: int(g.integers(k // 2, k + 1))])
+            sel[b, : pick.size] = pick
+            prev[b] = pick[pick < vl[b]]
+        sel_t = torch.from_numpy(sel).to(dev)
+        isa.sparse_gather_attn_decode(aa, sel_t, 1, k, 1, out, None, ws)
+        isa.sparse_hot_update(None, aa, sel_t, k, 1, S, step, slot_token, slot_stamp, ws)
+        torch.cuda.synchronize()
+        state = _oracle_all(state[0], state[1], state[2], state[3], host_bits, sel, vl, step)
+        _check((hot_slot, slot_token, slot_stamp, hot_kv), state, f"step {step}")
+
+
+def test_hot_update_after_fused_step():
+    w = synth.get("hot_small")
+    print(f"[hot-update] fused step on {w.name}", flush=True)
+    inp = synth.make_inputs(w, "cuda")
+    # start from the buffer the data generator builds for the workload's own
+    # selection (index scores and top-k through the library), then let the
+    # update evolve it over two steps
+    ia = isa.lightning_index_args(inp["q_idx"], inp["head_w"], inp["k8"], inp["k_scale"],
+                                  inp.get("seq_lens"))
+    scores = torch.empty((w.B, w.n), dtype=torch.float32, device="cuda")
+    ws0 = isa.workspace(max(isa.sparse_workspace_size(ia, None, w.k),
+                            isa.sparse_topk_workspace_size(w.B, w.n, w.k)))
+    isa.sparse_index_score(ia, scores, ws0)
+    sel0 = torch.empty((w.B, w.k), dtype=torch.int32, device="cuda")
+    isa.sparse_topk(scores, w.k, sel0, None, inp.get("seq_lens"), 1, ws0)
+    torch.cuda.synchronize()
+    hot = build_hot_buffer(inp, sel0, "cuda")
+    r = StepRunner(inp, hot=hot)
+    S = w.hot
+    hs = hot["hot_slot"]
+    slot_token = torch.full((w.B, S), -1, dtype=torch.int32, device="cuda")
+    stt = slot_token.cpu().numpy()
+    hsn = hs.cpu().numpy()
+    for b in range(w.B):
+        for t in np.nonzero(hsn[b] >= 0)[0]:
+            stt[b, hsn[b, t]] = t
+    slot_token.copy_(torch.from_numpy(stt))
+    slot_stamp = torch.zeros((w.B, S), dtype=torch.int32, device="cuda")
+    host_bits = hot["host_kv"].view(torch.int16).numpy().view(np.uint16)
+    vl = np.array([w.valid(b) for b in range(w.B)])
+    aa = r.layer_args[0][0]
+    for step in (1, 2):
+        state = (hs.cpu().numpy(), slot_token.cpu().numpy(), slot_stamp.cpu().numpy(),
+                 _bits(hot["hot_kv"]))
+        r.run()
+        isa.sparse_hot_update(r.ia, aa, r.topk, w.k, 1, S, step, slot_token, slot_stamp, r.ws)
+        torch.cuda.synchronize()
+        sel = r.topk[:, 0].cpu().numpy()
+        ref = _oracle_all(*state, host_bits, sel, vl, step)
+        _check((hs, slot_token, slot_stamp, hot["hot_kv"]), ref, f"fused step {step}")
+        # every selected token is resident after the update (the buffer holds more)
+        for b in range(w.B):
+            s = sel[b][(sel[b] >= 0) & (sel[b] < vl[b])]
+            assert (ref[0][b, s] >= 0).all()
