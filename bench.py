@@ -187,6 +187,11 @@ def main() -> int:
                     help="Fathom workloads: bit planes read in place from pinned host memory")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run the known-size copy that hardware byte counters are scaled by")
+    ap.add_argument("--policy", choices=["lru"], default=None,
+                    help="hot-buffer workloads: evolve the hot buffer with the least-recently-used "
+                         "replacement (sparse_hot_update) over steps whose index queries drift")
+    ap.add_argument("--drift", type=float, default=0.1,
+                    help="--policy: per-step query drift q <- (1 - a) q + a noise")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -196,6 +201,8 @@ def main() -> int:
 
     if args.calibrate_copy:
         return calibrate_copy()
+    if args.policy:
+        return run_policy(args)
 
     import torch
 
@@ -353,6 +360,99 @@ def time_append(w, r, stream) -> dict:
     e1.record(stream)
     torch.cuda.synchronize()
     return {"us_per_call": round(e0.elapsed_time(e1) / reps * 1e3, 2), "tokens": w.B}
+
+
+def run_policy(args) -> int:
+    """Hot-buffer workloads with the replacement policy: steps (eager, since
+    each update carries its own step number) whose index queries drift, each
+    followed by sparse_hot_update.  Reports steps/s of step + update, the
+    update's own time and the miss rate the policy leaves."""
+    import torch
+
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    import synth
+    from synth.gen import build_hot_buffer
+    import indexer_top_sparse_amd as isa
+    from indexer_top_sparse_amd.runner import StepRunner
+
+    isa.lib()
+    w = synth.get(args.config)
+    if not w.hot:
+        print("--policy needs a hot-buffer workload", file=sys.stderr)
+        return 2
+    dev = "cuda"
+    inp = synth.make_inputs(w, dev)
+    # the starting buffer: the first selection, at the workload's miss rate
+    hot = build_hot_buffer(inp, _selection_for_hot(inp, w, dev), dev)
+    r = StepRunner(inp, hot=hot)
+    S = w.hot
+    hs = hot["hot_slot"]
+    toks = torch.full((w.B, S), -1, dtype=torch.int32, device=dev)
+    bi, ti = torch.nonzero(hs >= 0, as_tuple=True)
+    toks[bi, hs[bi, ti].long()] = ti.to(torch.int32)
+    stamps = torch.zeros((w.B, S), dtype=torch.int32, device=dev)
+    aa = r.layer_args[0][0]
+    q = inp["q_idx"]
+    g = torch.Generator(device=dev)
+    g.manual_seed(w.seed + 555)
+    args.warmup = max(args.warmup, 1)
+    total = args.warmup + args.steps
+    qs = []
+    for _ in range(total):
+        noise = torch.randn(q.shape, generator=g, device=dev, dtype=torch.float32)
+        q.copy_(((1.0 - args.drift) * q.float() + args.drift * noise).to(q.dtype))
+        qs.append(q.clone())
+    misses = torch.zeros((), dtype=torch.int64, device=dev)
+    selected = torch.zeros((), dtype=torch.int64, device=dev)
+    seq = inp.get("seq_lens")
+    vl = (seq if seq is not None else torch.full((w.B,), w.n, device=dev)).view(-1, 1)
+    upd = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+
+    def step(i, timed):
+        q.copy_(qs[i])
+        r.run()
+        sel = r.topk[:, 0]
+        ok = (sel >= 0) & (sel < vl)
+        hit = torch.gather(hs, 1, sel.clamp(min=0).long()) >= 0
+        misses.add_((ok & ~hit).sum())
+        selected.add_(ok.sum())
+        if timed:
+            upd[i - args.warmup][0].record()
+        isa.sparse_hot_update(r.ia, aa, r.topk, w.k, 1, S, i + 1, toks, stamps, r.ws)
+        if timed:
+            upd[i - args.warmup][1].record()
+
+    print(f"[bench] {w.name}: {args.warmup} + {args.steps} steps with LRU replacement",
+          file=sys.stderr, flush=True)
+    # warm-up steps run every kernel the timed ones do (first launches load code)
+    for i in range(max(args.warmup, 1)):
+        step(i, False)
+    torch.cuda.synchronize()
+    misses.zero_()
+    selected.zero_()
+    # timed steps; the miss count (three small reductions per step) and the
+    # update's events ride along
+    t0 = time.perf_counter()
+    for i in range(args.warmup, total):
+        step(i, True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    upd_us = sum(a.elapsed_time(b) for a, b in upd) / len(upd) * 1e3
+    line = {
+        "metric": METRIC + " (hot buffer with LRU replacement)",
+        "value": round(args.steps / elapsed, 2), "unit": "steps/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(1e3 * elapsed / args.steps, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.B, "context": w.n, "top_k": w.k,
+                   "hot_tokens": S, "policy": args.policy, "drift": args.drift,
+                   "start_miss_rate": w.miss_rate, "graph": False},
+        "measured_miss_rate": round(misses.item() / max(selected.item(), 1), 4),
+        "update_us_per_call": round(upd_us, 2),
+    }
+    print(json.dumps(line), flush=True)
+    return 0
 
 
 def _selection_for_hot(inp, w, dev):
