@@ -9,6 +9,8 @@ a step, against the oracle (oracle/hot.py), bit for bit.
   that stay out) and ties of stamps.  After every update the token -> slot
   map, the slot -> token map, the stamps and every hot row are compared with
   the oracle's.
+* 64-token selection units (the tokens of the selected blocks), more misses
+  than free slots.
 * The fused step (sparse_decode_step, lightning indexer) on the small
   hot-buffer workload, then the update with the step's own selection.
 """
@@ -107,6 +109,52 @@ def test_hot_update_sequence_matches_oracle(B, n, S, k, steps, valid):
         torch.cuda.synchronize()
         state = _oracle_all(state[0], state[1], state[2], state[3], host_bits, sel, vl, step)
         _check((hot_slot, slot_token, slot_stamp, hot_kv), state, f"step {step}")
+
+
+def test_hot_update_block_units():
+    # 64-token selection units: the misses are the tokens of the selected
+    # blocks (block order, then token order) that the buffer does not hold
+    B, n, S, kb, unit, d, Hq = 2, 3000, 512, 12, 64, 576, 64
+    print(f"[hot-update] block units B={B} n={n} slots={S} blocks={kb}", flush=True)
+    g = np.random.default_rng(77)
+    vl = np.array([3000, 1500])
+    host = torch.from_numpy(g.normal(size=(B, n, d)).astype(np.float32)).to(torch.bfloat16).pin_memory()
+    host_bits = host.view(torch.int16).numpy().view(np.uint16)
+    hs = np.full((B, n), -1, np.int32)
+    st = np.full((B, S), -1, np.int32)
+    ss = np.full((B, S), -1, np.int32)
+    hk = np.zeros((B, S, d), np.uint16)
+    for b in range(B):
+        toks = g.choice(vl[b], size=300, replace=False)
+        for s_, t in enumerate(toks):
+            hs[b, t], st[b, s_], ss[b, s_] = s_, t, int(g.integers(0, 5))
+            hk[b, s_] = host_bits[b, t]
+    dev = "cuda"
+    hot_slot = torch.from_numpy(hs).to(dev)
+    slot_token = torch.from_numpy(st).to(dev)
+    slot_stamp = torch.from_numpy(ss).to(dev)
+    hot_kv = torch.from_numpy(hk.view(np.int16)).to(dev).view(torch.bfloat16)
+    q = torch.from_numpy(g.normal(size=(B, Hq, d)).astype(np.float32) * 0.1).to(torch.bfloat16).to(dev)
+    seq = torch.from_numpy(vl.astype(np.int32)).to(dev)
+    aa = isa.attn_args(q, None, n=n, seq_lens=seq, sm_scale=d ** -0.5,
+                       hot_slot=hot_slot, hot_kv=hot_kv, host_kv=host)
+    ws = isa.workspace(isa.sparse_workspace_size(None, aa, kb * unit))
+    out = torch.empty((B, Hq, 512), dtype=torch.float32, device=dev)
+    nblk = (n + unit - 1) // unit
+    sel = np.full((B, kb), -1, np.int32)
+    for b in range(B):
+        sel[b, :10] = np.sort(g.choice(nblk, size=10, replace=False))
+    sel_t = torch.from_numpy(sel).to(dev)
+    isa.sparse_gather_attn_decode(aa, sel_t, 1, kb, unit, out, None, ws)
+    isa.sparse_hot_update(None, aa, sel_t, kb, unit, S, 9, slot_token, slot_stamp, ws)
+    torch.cuda.synchronize()
+    toks = np.full((B, kb * unit), -1, np.int64)
+    for b in range(B):
+        for j in range(kb * unit):
+            u = sel[b, j // unit]
+            toks[b, j] = -1 if u < 0 else u * unit + j % unit
+    ref = _oracle_all(hs, st, ss, hk, host_bits, toks, vl, 9)
+    _check((hot_slot, slot_token, slot_stamp, hot_kv), ref, "block units")
 
 
 def test_hot_update_after_fused_step():
