@@ -504,18 +504,21 @@ __global__ __launch_bounds__(kMlaThreads, 1) void attn_mla_kernel(AttnPlan p) {
       // the eight tokens of its k range; lane n of each group addresses
       // token row n / 4 of the four and columns 4 (n % 4) .. +3
       const uint16_t* vb = kt + (4 * g + (n >> 2)) * kMlaRow + 128 * cq + 4 * (n & 3);
+      bf16x8 vas[8];
 #pragma unroll
       for (int mc = 0; mc < 8; ++mc) {
         const s16x4 r0 = lds_read_tr16(vb + 16 * mc);
         const s16x4 r1 = lds_read_tr16(vb + 16 * kMlaRow + 16 * mc);
-        const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7));
+        vas[mc] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+#pragma unroll
+      for (int mc = 0; mc < 8; ++mc) {
 #pragma unroll
         for (int hb = 0; hb < 4; ++hb)
-          o[hb][mc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pbk[hb], o[hb][mc], 0, 0, 0);
+          o[hb][mc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vas[mc], pbk[hb], o[hb][mc], 0, 0, 0);
 #pragma unroll
         for (int hb = 0; hb < 4; ++hb)
-          o[hb][mc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pbl[hb], o[hb][mc], 0, 0, 0);
-        if ((mc & 3) == 3) __builtin_amdgcn_sched_barrier(0);  // bound the live V fragments
+          o[hb][mc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vas[mc], pbl[hb], o[hb][mc], 0, 0, 0);
       }
     };
     prologue();
