@@ -164,7 +164,8 @@ def cpu_baseline(w, inp, requests: int) -> dict:
             "kind": "oracle",
             "sample": f"{len(reqs)} of {w.B} requests at full context "
                       f"(n={w.n}, k={w.k}), oracle seconds scaled by {w.B}/{len(reqs)}; "
-                      f"host cpu_count={os.cpu_count()}"}
+                      f"host cpu_count={os.cpu_count()}, "
+                      f"affinity={len(os.sched_getaffinity(0))}, BLAS threads={threads}"}
 
 
 def main() -> int:
