@@ -99,10 +99,26 @@ int attn_splits(const sparse_attn_args& a, int k_tokens) {
     min_tok = 16;
     target = 256;
   } else if (a.d_qk == 576) {
-    // one 8-wave workgroup per compute unit, 64 heads each
-    groups = a.n_q_heads / 64;
-    min_tok = 256;
-    target = 256;
+    // One 8-wave workgroup per compute unit (its LDS), 64 heads each, so the
+    // workgroups run in rounds of one per CU.  A workgroup costs about six
+    // 32-token tiles of fixed time (row table, pipeline fill, epilogue) plus
+    // its tiles, and any split adds the combine (about four tiles): take the
+    // split count with the least rounds x per-workgroup time.
+    constexpr int kCUs = 256;  // MI355X
+    const int64_t base = (int64_t)std::max(a.batch, 1) * std::max(a.n_q_heads / 64, 1);
+    const int64_t tiles = ceil_div(k_tokens, 32);
+    const int64_t s_min = std::max<int64_t>(1, ceil_div(k_tokens, 2048));
+    const int64_t s_max = std::max<int64_t>(s_min, std::min<int64_t>(64, k_tokens / 256));
+    int64_t best = s_min, best_cost = -1;
+    for (int64_t sp = s_min; sp <= s_max; ++sp) {
+      const int64_t rounds = ceil_div(base * sp, kCUs);
+      const int64_t cost = rounds * (ceil_div(tiles, sp) + 6) + (sp > 1 ? 4 : 0);
+      if (best_cost < 0 || cost < best_cost) {
+        best = sp;
+        best_cost = cost;
+      }
+    }
+    return (int)best;
   } else {
     // two 4-wave workgroups per compute unit, KV head each
     groups = a.n_kv_heads;
