@@ -450,13 +450,14 @@ __global__ __launch_bounds__(kLtThreads) void score_lightning_kernel(
 }
 
 // long spans per workgroup (fewer histogram clears and stores) when the
-// batch still gives at least two workgroups per compute unit
+// batch still gives about two workgroups per compute unit (448: 1.75 per unit
+// already beats four times as many short spans)
 constexpr int kLtLong = 64, kLtShort = 16;
 static_assert(kLtLong * kLtStride <= kHistPartMax, "histogram part overflow");
 bool lightning_long(const sparse_index_args& a) {
   const int64_t long_wgs =
       (int64_t)a.batch * ((a.n + kLtLong * kLtStride - 1) / (kLtLong * kLtStride));
-  return long_wgs >= 512;
+  return long_wgs >= 448;
 }
 int lightning_parts(const sparse_index_args& a) {
   const int span = (lightning_long(a) ? kLtLong : kLtShort) * kLtStride;
