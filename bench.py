@@ -171,7 +171,7 @@ def cpu_baseline(w, inp, requests: int) -> dict:
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="lightning_128k")
     ap.add_argument("--no-graph", action="store_true")
