@@ -195,8 +195,8 @@ def main() -> int:
                     help="--policy: per-step query drift q <- (1 - a) q + a noise")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(requests shard by batch with no exchange; see the sharding notes)",
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
+              "(requests would shard by batch with no exchange between GPUs)",
               file=sys.stderr)
         return 2
 

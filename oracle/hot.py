@@ -6,8 +6,8 @@ TEST INFRASTRUCTURE ONLY: nothing in the product path imports this module.
 X-Mem" (Figure 1 and the decode-path list) has decode GPUs keep a hot KV
 buffer per request and layer in HBM and fetch only the missing selected rows;
 it keeps HiSparse's cache management but measures fixed miss rates with
-prefetch off, and states no replacement rule.  The rule this build reads
-(least recently used, the plainest cache policy) is, per request, after a
+prefetch off, and states no replacement rule.  The rule taken here (least
+recently used, the plainest cache policy) is, per request, after a
 step that selected the tokens T (selection order, padding and tokens past the
 valid length dropped):
 
