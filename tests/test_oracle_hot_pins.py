@@ -9,12 +9,17 @@
   has room, moved rows are the host rows, and no evicted slot was more
   recently used (stamp, slot index) than a surviving slot that this step did
   not select.
+* the prefetch: a worked example computed by hand from its rule, agreement
+  with the update on every state where no candidate is resident (the two
+  rules then coincide), and on random states the map invariants, resident
+  candidates and this step's slots left alone, and the LRU order of the
+  replaced slots.
 """
 from collections import OrderedDict
 
 import numpy as np
 
-from oracle.hot import hot_update
+from oracle.hot import hot_prefetch, hot_update
 
 
 def _state(S, n, d=3):
@@ -113,4 +118,93 @@ def test_random_invariants():
         untouched = [s for s in range(S) if st2[s] == st[s] and ss2[s] < step]
         for r in replaced:
             for u in untouched:
+                assert (ss[r], r) < (ss[u], u)
+
+
+def test_prefetch_worked_example():
+    # slots: 0 holds 10 (stamped this step, 3), 1 holds 11 (stamp 1), 2 is
+    # empty, 3 holds 12 (stamp 0), 4 holds 13 (stamp 2).  Candidates 11 and
+    # 10 are resident (slot 1 is protected, slot 0 is this step's); 40 is
+    # past the valid length.  The fills 20, 21, 22, 23 can use slots 2, 3, 4
+    # only: in slot order 20 -> 2, 21 -> 3 (evicting 12), 22 -> 4 (evicting
+    # 13), and 23 stays out.
+    n, S, valid = 48, 5, 32
+    hs, st, ss, hk = _state(S, n)
+    host = _host(n)
+    for s_, (t, stamp) in enumerate([(10, 3), (11, 1), (None, -1), (12, 0), (13, 2)]):
+        if t is not None:
+            hs[t], st[s_], hk[s_] = s_, t, host[t]
+        ss[s_] = stamp
+    hs2, st2, ss2, hk2 = hot_prefetch(hs, st, ss, hk, host, [11, 20, 21, 22, 23, -1, 40, 10],
+                                      valid, 3)
+    assert st2.tolist() == [10, 11, 20, 21, 22]
+    assert ss2.tolist() == [3, 1, 3, 3, 3]
+    assert hs2[12] == -1 and hs2[13] == -1 and hs2[23] == -1 and hs2[40] == -1
+    assert hs2[11] == 1 and hs2[10] == 0
+    assert hs2[20] == 2 and hs2[21] == 3 and hs2[22] == 4
+    for s_ in (2, 3, 4):
+        assert (hk2[s_] == host[st2[s_]]).all()
+
+
+def _random_state(g, n, S, step):
+    hs, st, ss, hk = _state(S, n)
+    host = _host(n)
+    res = g.choice(n, size=int(g.integers(0, min(S, n) + 1)), replace=False)
+    slots = g.choice(S, size=res.shape[0], replace=False)
+    for t, s in zip(res, slots):
+        hs[t], st[s], hk[s] = s, t, host[t]
+    # stamps from -1 up to step itself (a slot this step already used)
+    ss[:] = g.integers(-1, step + 1, size=S)
+    return hs, st, ss, hk, host
+
+
+def test_prefetch_equals_update_without_resident_candidates():
+    g = np.random.default_rng(23)
+    for case in range(300):
+        n = int(g.integers(8, 200))
+        S = int(g.integers(1, 40))
+        valid = int(g.integers(1, n + 1))
+        step = int(g.integers(1, 30))
+        hs, st, ss, hk, host = _random_state(g, n, S, step)
+        free = np.nonzero(hs < 0)[0]
+        cand = g.permutation(free)[: int(g.integers(0, free.shape[0] + 1))].copy()
+        cand[g.random(cand.shape[0]) < 0.1] = -1
+        a = hot_prefetch(hs, st, ss, hk, host, cand, valid, step)
+        b = hot_update(hs, st, ss, hk, host, cand, valid, step)
+        for x, y in zip(a, b):
+            assert np.array_equal(x, y), case
+
+
+def test_prefetch_random_invariants():
+    g = np.random.default_rng(29)
+    for case in range(300):
+        n = int(g.integers(8, 200))
+        S = int(g.integers(1, 40))
+        valid = int(g.integers(1, n + 1))
+        step = int(g.integers(1, 30))
+        hs, st, ss, hk, host = _random_state(g, n, S, step)
+        cand = g.choice(n, size=int(g.integers(1, min(n, 40) + 1)), replace=False)
+        cand[g.random(cand.shape[0]) < 0.1] = -1
+        hs2, st2, ss2, hk2 = hot_prefetch(hs, st, ss, hk, host, cand, valid, step)
+        for s in range(S):
+            if st2[s] >= 0:
+                assert hs2[st2[s]] == s
+                assert (hk2[s] == host[st2[s]]).all()
+        for t in range(n):
+            if hs2[t] >= 0:
+                assert st2[hs2[t]] == t
+        chosen = [int(t) for t in cand if 0 <= t < valid]
+        held = {int(hs[t]) for t in chosen if hs[t] >= 0}
+        fills = [t for t in chosen if hs[t] < 0]
+        # resident candidates and slots this step already used keep everything
+        for s in held | {s for s in range(S) if ss[s] >= step}:
+            assert st2[s] == st[s] and ss2[s] == ss[s] and (hk2[s] == hk[s]).all()
+        eligible = [s for s in range(S) if ss[s] < step and s not in held]
+        if len(fills) <= len(eligible):
+            assert all(hs2[t] >= 0 and ss2[hs2[t]] == step for t in fills)
+        replaced = [s for s in range(S) if st2[s] != st[s]]
+        assert len(replaced) == min(len(fills), len(eligible))
+        kept = [s for s in eligible if s not in replaced]
+        for r in replaced:
+            for u in kept:
                 assert (ss[r], r) < (ss[u], u)
