@@ -193,6 +193,9 @@ def main() -> int:
                          "replacement (sparse_hot_update) over steps whose index queries drift")
     ap.add_argument("--drift", type=float, default=0.1,
                     help="--policy: per-step query drift q <- (1 - a) q + a noise")
+    ap.add_argument("--prefetch", type=int, default=0,
+                    help="--policy: after each update, prefetch the M tokens ranked just "
+                         "below the top-k (a top-(k+M) of the same scores)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on one GPU only: the library has no multi-GPU path "
@@ -366,8 +369,10 @@ def time_append(w, r, stream) -> dict:
 def run_policy(args) -> int:
     """Hot-buffer workloads with the replacement policy: steps (eager, since
     each update carries its own step number) whose index queries drift, each
-    followed by sparse_hot_update.  Reports steps/s of step + update, the
-    update's own time and the miss rate the policy leaves."""
+    followed by sparse_hot_update and, with --prefetch M, by
+    sparse_hot_prefetch of the M tokens ranked just below the top-k.
+    Reports steps/s of step + update (+ prefetch), the update's and the
+    prefetch's own times and the miss rate the policy leaves."""
     import torch
 
     sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
@@ -410,9 +415,25 @@ def run_policy(args) -> int:
     upd = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
 
+    M = args.prefetch
+    if M:
+        # the decomposed step keeps the scores, whose top-(k+M) names the
+        # prefetch candidates; its top-k runs in a workspace of its own so
+        # that the staged rows survive until the update
+        r.index_scores()
+        ws_t = isa.workspace(isa.sparse_topk_workspace_size(w.B, w.n, w.k + M))
+        cand = torch.empty((w.B, w.k + M), dtype=torch.int32, device=dev)
+        pf = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+
     def step(i, timed):
         q.copy_(qs[i])
-        r.run()
+        if M:
+            sc = r.index_scores()[:, 0]
+            isa.sparse_topk(sc, w.k, r.topk[:, 0], None, seq, 1, ws_t)
+            isa.sparse_gather_attn_decode(aa, r.topk, 1, w.k, 1, r.outs[0], r.lses[0], r.ws)
+        else:
+            r.run()
         sel = r.topk[:, 0]
         ok = (sel >= 0) & (sel < vl)
         hit = torch.gather(hs, 1, sel.clamp(min=0).long()) >= 0
@@ -420,9 +441,17 @@ def run_policy(args) -> int:
         selected.add_(ok.sum())
         if timed:
             upd[i - args.warmup][0].record()
-        isa.sparse_hot_update(r.ia, aa, r.topk, w.k, 1, S, i + 1, toks, stamps, r.ws)
+        isa.sparse_hot_update(None if M else r.ia, aa, r.topk, w.k, 1, S, i + 1, toks,
+                              stamps, r.ws)
         if timed:
             upd[i - args.warmup][1].record()
+        if M:
+            isa.sparse_topk(sc, w.k + M, cand, None, seq, 1, ws_t)
+            if timed:
+                pf[i - args.warmup][0].record()
+            isa.sparse_hot_prefetch(aa, cand, w.k + M, S, i + 1, toks, stamps)
+            if timed:
+                pf[i - args.warmup][1].record()
 
     print(f"[bench] {w.name}: {args.warmup} + {args.steps} steps with LRU replacement",
           file=sys.stderr, flush=True)
@@ -440,6 +469,7 @@ def run_policy(args) -> int:
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     upd_us = sum(a.elapsed_time(b) for a, b in upd) / len(upd) * 1e3
+    pf_us = sum(a.elapsed_time(b) for a, b in pf) / len(pf) * 1e3 if M else None
     line = {
         "metric": METRIC + " (hot buffer with LRU replacement)",
         "value": round(args.steps / elapsed, 2), "unit": "steps/s", "n_gpus": 1,
@@ -448,9 +478,10 @@ def run_policy(args) -> int:
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w.name, "batch": w.B, "context": w.n, "top_k": w.k,
                    "hot_tokens": S, "policy": args.policy, "drift": args.drift,
-                   "start_miss_rate": w.miss_rate, "graph": False},
+                   "start_miss_rate": w.miss_rate, "prefetch": M, "graph": False},
         "measured_miss_rate": round(misses.item() / max(selected.item(), 1), 4),
         "update_us_per_call": round(upd_us, 2),
+        "prefetch_us_per_call": round(pf_us, 2) if M else None,
     }
     print(json.dumps(line), flush=True)
     return 0

@@ -307,6 +307,31 @@ int sparse_hot_update(const sparse_index_args* ia, const sparse_attn_args* aa,
                       int32_t* slot_stamp, void* ws, size_t ws_bytes,
                       void* stream);
 
+/* Hot-buffer prefetch: preload rows the next steps are likely to select
+ * ([XM] the paragraph on X-Mem's APIs: HiSparse's prefetch mechanism is
+ * kept, without being stated, and every measured run has it off;
+ * CXL-SpecKV's abstract: speculative preloading of the entries future
+ * tokens will use).  The caller names the candidates, e.g. the tokens
+ * ranked just below the step's top-k (a top-(k+m) selection holds them).
+ * Run it after sparse_hot_update with the same step.  Per request:
+ *   - a resident candidate is left as it is: not replaced by this call and
+ *     not stamped;
+ *   - the other candidates, in list order, take the slots that are neither
+ *     stamped step nor holding a resident candidate, smallest (stamp, slot
+ *     index) first, in ascending slot order: the slot's previous token
+ *     loses its slot (hot_slot -1), the candidate's row is copied from
+ *     host_kv (over PCIe) into hot_kv, hot_slot of the candidate becomes
+ *     the slot, and the slot is stamped step;
+ *   - candidates beyond the slots available stay out.
+ * aa: the hot-buffer attention arguments (hot_slot, hot_kv, host_kv, n,
+ * seq_lens); cand: [B][m] distinct token ids, -1 padding, tokens at or past
+ * the valid length ignored; m: 1..4096; n_slots, step, slot_token and
+ * slot_stamp as for sparse_hot_update, updated in place.  No workspace.
+ * Errors as for sparse_hot_update; nothing is launched on an error. */
+int sparse_hot_prefetch(const sparse_attn_args* aa, const int32_t* cand, int32_t m,
+                        int32_t n_slots, int32_t step, int32_t* slot_token,
+                        int32_t* slot_stamp, void* stream);
+
 /* Device-visible address of pinned host memory allocated with
  * hipHostMalloc (e.g. a pinned torch tensor); used for host_kv. */
 int sparse_host_device_pointer(void* host_ptr, void** dev_ptr);

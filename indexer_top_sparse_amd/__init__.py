@@ -94,10 +94,12 @@ def lib() -> ctypes.CDLL:
         L.sparse_append_token.argtypes = [P(IndexArgs), P(AttnArgs), _vp, _vp, _vp, _vp, _vp]
         L.sparse_hot_update.argtypes = [P(IndexArgs), P(AttnArgs), _vp, _i32, _i32, _i32,
                                         _i32, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+        L.sparse_hot_prefetch.argtypes = [P(AttnArgs), _vp, _i32, _i32, _i32, _vp, _vp, _vp]
         for f in ("sparse_workspace_size", "sparse_topk_workspace_size",
                   "sparse_read_depth", "sparse_index_score", "sparse_topk",
                   "sparse_gather_attn_decode", "sparse_decode_step",
-                  "sparse_host_device_pointer", "sparse_append_token", "sparse_hot_update"):
+                  "sparse_host_device_pointer", "sparse_append_token", "sparse_hot_update",
+                  "sparse_hot_prefetch"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -352,6 +354,20 @@ def sparse_hot_update(ia: _Holder | None, aa: _Holder, sel: torch.Tensor, k: int
     _check(lib().sparse_hot_update(ia.ref() if ia is not None else None, aa.ref(), _p(sel),
                                    k, sel_unit, n_slots, step, _p(slot_token),
                                    _p(slot_stamp), _p(ws), ws.numel(), _stream(stream)))
+
+
+def sparse_hot_prefetch(aa: _Holder, cand: torch.Tensor, m: int, n_slots: int, step: int,
+                        slot_token: torch.Tensor, slot_stamp: torch.Tensor,
+                        stream=None) -> None:
+    """Preload the non-resident tokens of `cand` ([B][m] int32, -1 padding)
+    into the hot buffer of `aa`, least recently used slots first, never
+    replacing a slot stamped `step` or a resident candidate; rows come from
+    aa's pinned host KV.  slot_token / slot_stamp as for sparse_hot_update."""
+    for t in (cand, slot_token, slot_stamp):
+        if not t.is_contiguous() or t.dtype != torch.int32:
+            raise ValueError("cand / slot_token / slot_stamp must be contiguous int32")
+    _check(lib().sparse_hot_prefetch(aa.ref(), _p(cand), m, n_slots, step, _p(slot_token),
+                                     _p(slot_stamp), _stream(stream)))
 
 
 def host_device_pointer(host: torch.Tensor) -> int:

@@ -620,6 +620,34 @@ int sparse_hot_update(const sparse_index_args* ia, const sparse_attn_args* aa,
   return SPARSE_OK;
 }
 
+int sparse_hot_prefetch(const sparse_attn_args* aa, const int32_t* cand, int32_t m,
+                        int32_t n_slots, int32_t step, int32_t* slot_token,
+                        int32_t* slot_stamp, void* stream) {
+  int rc = check_attn(aa, 1, m, 1);
+  if (rc) return rc;
+  CHECK(aa->hot_slot, SPARSE_EINVAL, "hot_slot NULL: no hot buffer to prefetch into");
+  CHECK(n_slots >= 1 && n_slots <= sd::kHotMaxSlots, SPARSE_EUNSUPPORTED,
+        "n_slots %d outside 1..%d", n_slots, sd::kHotMaxSlots);
+  CHECK(step >= 0, SPARSE_EINVAL, "step %d < 0", step);
+  CHECK(m <= sd::kHotMaxSel, SPARSE_EUNSUPPORTED, "%d candidates above %d", m,
+        sd::kHotMaxSel);
+  if (aa->batch == 0) return SPARSE_OK;
+  CHECK(cand && slot_token && slot_stamp, SPARSE_EINVAL, "cand / slot_token / slot_stamp NULL");
+  sd::HotPlan p;
+  p.a = *aa;
+  p.sel = cand;
+  p.k = m;
+  p.sel_unit = 1;
+  p.k_tokens = m;
+  p.n_slots = n_slots;
+  p.step = step;
+  p.slot_token = slot_token;
+  p.slot_stamp = slot_stamp;
+  p.staging = nullptr;  // prefetch: rows from host_kv
+  HIPCHECK(sd::launch_hot_update(p, (hipStream_t)stream));
+  return SPARSE_OK;
+}
+
 int sparse_host_device_pointer(void* host_ptr, void** dev_ptr) {
   CHECK(host_ptr && dev_ptr, SPARSE_EINVAL, "NULL pointer");
   HIPCHECK(hipHostGetDevicePointer(dev_ptr, host_ptr, 0));

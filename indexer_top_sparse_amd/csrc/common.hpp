@@ -253,7 +253,8 @@ struct HotPlan {
   int n_slots, step;
   int32_t* slot_token;         // [B][n_slots] token held, or -1
   int32_t* slot_stamp;         // [B][n_slots] step of the last use
-  const uint16_t* staging;     // [B][k_tokens][d_qk] the step's fetched rows
+  const uint16_t* staging;     // [B][k_tokens][d_qk] the step's fetched rows;
+                               // NULL: a prefetch, rows from host_kv
 };
 hipError_t launch_hot_update(const HotPlan& p, hipStream_t s);
 hipError_t launch_append(const sparse_index_args* ia, const sparse_attn_args* aa,

@@ -20,6 +20,18 @@
 //      histograms, the digit found by one wave), then the victims in slot
 //      order: keys below it, and the lowest slots among the keys equal to it;
 //   3. the maps are updated, the staged rows copied and the stamps written.
+//
+// The same kernel runs the prefetch (staging NULL), which preloads rows the
+// next steps are likely to select.  The pages keep HiSparse's prefetch
+// mechanism without stating it, and CXL-SpecKV's abstract names speculative
+// preloading of the entries future tokens will use; here the caller names
+// the candidates (e.g. the tokens ranked just below the top-k), and:
+//   * a resident candidate is left as it is (neither replaced nor stamped);
+//   * the other candidates, in list order, take the slots neither stamped
+//     `step` nor holding a resident candidate, smallest (stamp, slot) first,
+//     in ascending slot order; rows come from the pinned host KV and the
+//     filled slots are stamped `step`;
+//   * candidates beyond the slots available stay out.
 #include "common.hpp"
 
 namespace sd {
@@ -47,6 +59,10 @@ __global__ __launch_bounds__(kHotThreads) void hot_update_kernel(HotPlan p) {
   int32_t* ss = p.slot_stamp + (int64_t)b * S;
   const int32_t* selrow = p.sel + (int64_t)b * p.k;
   const int valid = valid_tokens(A, b);
+  const bool prefetch = p.staging == nullptr;
+  // a hit is stamped by the update; a resident prefetch candidate is only
+  // kept out of the eligible set
+  const uint32_t hit_key = prefetch ? kKeyLater : kKeyUsed;
 
   for (int s = tid; s < S; s += kHotThreads) {
     const int32_t stamp = ss[s];
@@ -65,7 +81,7 @@ __global__ __launch_bounds__(kHotThreads) void hot_update_kernel(HotPlan p) {
       if (t >= 0) {
         const int s = hs[t];
         if (s < 0) miss = true;
-        else if (s < S) key_s[s] = kKeyUsed;  // (a slot past S is not ours to touch)
+        else if (s < S) key_s[s] = hit_key;  // (a slot past S is not ours to touch)
       }
     }
     int total;
@@ -158,12 +174,22 @@ __global__ __launch_bounds__(kHotThreads) void hot_update_kernel(HotPlan p) {
       key_s[v] = kKeyUsed;
     }
     const int cpr = A.d_qk * 2 / 16;  // 16-byte chunks per row
-    const char* stage = (const char*)(p.staging + (int64_t)b * K * A.d_qk);
     char* hot = (char*)A.hot_kv + (int64_t)b * A.hot_stride_b * 2;
-    for (int q = tid; q < need * cpr; q += kHotThreads) {
-      const int i = q / cpr, c = q % cpr;
-      const uint4 x = *(const uint4*)(stage + ((int64_t)mpos_s[i] * A.d_qk * 2 + 16 * c));
-      *(uint4*)(hot + (int64_t)vic_s[i] * A.hot_stride_s * 2 + 16 * c) = x;
+    if (prefetch) {
+      // rows straight from the pinned host KV (device alias, over PCIe)
+      const char* host = (const char*)A.host_kv + (int64_t)b * A.host_stride_b * 2;
+      for (int q = tid; q < need * cpr; q += kHotThreads) {
+        const int i = q / cpr, c = q % cpr;
+        const uint4 x = *(const uint4*)(host + ((int64_t)mtok_s[i] * A.host_stride_t * 2 + 16 * c));
+        *(uint4*)(hot + (int64_t)vic_s[i] * A.hot_stride_s * 2 + 16 * c) = x;
+      }
+    } else {
+      const char* stage = (const char*)(p.staging + (int64_t)b * K * A.d_qk);
+      for (int q = tid; q < need * cpr; q += kHotThreads) {
+        const int i = q / cpr, c = q % cpr;
+        const uint4 x = *(const uint4*)(stage + ((int64_t)mpos_s[i] * A.d_qk * 2 + 16 * c));
+        *(uint4*)(hot + (int64_t)vic_s[i] * A.hot_stride_s * 2 + 16 * c) = x;
+      }
     }
   }
   __syncthreads();

@@ -235,3 +235,26 @@ def test_hot_update_validation_codes():
                                FAKE, FAKE, big, None) == isa.SPARSE_EINVAL
     # an empty batch is a no-op
     assert L.sparse_hot_update(None, ctypes.byref(_hot_attn(B=0)), *ok) == isa.SPARSE_OK
+
+
+def test_hot_prefetch_validation_codes():
+    L = isa.lib()
+    a = _hot_attn()
+    f = L.sparse_hot_prefetch
+    # no hot buffer, no candidates, too many candidates
+    assert f(ctypes.byref(_mla_attn()), FAKE, 16, 64, 3, FAKE, FAKE, None) == isa.SPARSE_EINVAL
+    assert f(ctypes.byref(a), FAKE, 0, 64, 3, FAKE, FAKE, None) == isa.SPARSE_EINVAL
+    assert f(ctypes.byref(a), FAKE, 4097, 64, 3, FAKE, FAKE, None) == isa.SPARSE_EUNSUPPORTED
+    # slot count and step limits
+    assert f(ctypes.byref(a), FAKE, 16, 0, 3, FAKE, FAKE, None) == isa.SPARSE_EUNSUPPORTED
+    assert f(ctypes.byref(a), FAKE, 16, 8193, 3, FAKE, FAKE, None) == isa.SPARSE_EUNSUPPORTED
+    assert f(ctypes.byref(a), FAKE, 16, 64, -1, FAKE, FAKE, None) == isa.SPARSE_EINVAL
+    # NULL candidates or state
+    assert f(ctypes.byref(a), None, 16, 64, 3, FAKE, FAKE, None) == isa.SPARSE_EINVAL
+    assert f(ctypes.byref(a), FAKE, 16, 64, 3, FAKE, None, None) == isa.SPARSE_EINVAL
+    # no pinned host KV to read from
+    b = _hot_attn()
+    b.host_kv = None
+    assert f(ctypes.byref(b), FAKE, 16, 64, 3, FAKE, FAKE, None) == isa.SPARSE_EINVAL
+    # an empty batch is a no-op
+    assert f(ctypes.byref(_hot_attn(B=0)), FAKE, 16, 64, 3, FAKE, FAKE, None) == isa.SPARSE_OK

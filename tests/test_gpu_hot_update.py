@@ -13,6 +13,10 @@ a step, against the oracle (oracle/hot.py), bit for bit.
   than free slots.
 * The fused step (sparse_decode_step, lightning indexer) on the small
   hot-buffer workload, then the update with the step's own selection.
+* The prefetch (sparse_hot_prefetch) after each update of a sequence:
+  candidate lists that mix resident tokens, new tokens, padding and tokens
+  past the valid length, more candidates than free slots, against the
+  oracle's hot_prefetch.
 """
 import numpy as np
 import pytest
@@ -22,7 +26,7 @@ import indexer_top_sparse_amd as isa
 import synth
 from synth.gen import build_hot_buffer
 from indexer_top_sparse_amd.runner import StepRunner
-from oracle.hot import hot_update
+from oracle.hot import hot_prefetch, hot_update
 
 pytestmark = pytest.mark.gpu
 
@@ -201,3 +205,79 @@ def test_hot_update_after_fused_step():
         for b in range(w.B):
             s = sel[b][(sel[b] >= 0) & (sel[b] < vl[b])]
             assert (ref[0][b, s] >= 0).all()
+
+
+PF_CASES = [
+    # (B, n, slots, k, candidates, steps, valid lengths)
+    (3, 3000, 1024, 512, 300, 3, [3000, 2500, 700]),
+    (2, 2000, 160, 100, 120, 3, [2000, 90]),  # more candidates than free slots
+]
+
+
+@pytest.mark.parametrize("B,n,S,k,m,steps,valid", PF_CASES,
+                         ids=[f"S{c[2]}-m{c[4]}" for c in PF_CASES])
+def test_hot_prefetch_matches_oracle(B, n, S, k, m, steps, valid):
+    print(f"[hot-prefetch] B={B} n={n} slots={S} k={k} m={m} steps={steps}", flush=True)
+    g = np.random.default_rng(S + m + n)
+    Hq, d = 64, 576
+    vl = np.array(valid)
+    host = torch.from_numpy(g.normal(size=(B, n, d)).astype(np.float32)).to(torch.bfloat16).pin_memory()
+    host_bits = host.view(torch.int16).numpy().view(np.uint16)
+    hs = np.full((B, n), -1, np.int32)
+    st = np.full((B, S), -1, np.int32)
+    ss = np.full((B, S), -1, np.int32)
+    hk = np.zeros((B, S, d), np.uint16)
+    for b in range(B):
+        cnt = int(g.integers(0, min(S, vl[b]) + 1))
+        toks = g.choice(vl[b], size=cnt, replace=False)
+        slots = g.choice(S, size=cnt, replace=False)
+        for t, s_ in zip(toks, slots):
+            hs[b, t], st[b, s_], ss[b, s_] = s_, t, int(g.integers(-1, 6))
+            hk[b, s_] = host_bits[b, t]
+    dev = "cuda"
+    hot_slot = torch.from_numpy(hs).to(dev)
+    slot_token = torch.from_numpy(st).to(dev)
+    slot_stamp = torch.from_numpy(ss).to(dev)
+    hot_kv = torch.from_numpy(hk.view(np.int16)).to(dev).view(torch.bfloat16)
+    q = torch.from_numpy(g.normal(size=(B, Hq, d)).astype(np.float32) * 0.1).to(torch.bfloat16).to(dev)
+    seq = torch.from_numpy(vl.astype(np.int32)).to(dev)
+    aa = isa.attn_args(q, None, n=n, seq_lens=seq, sm_scale=d ** -0.5,
+                       hot_slot=hot_slot, hot_kv=hot_kv, host_kv=host)
+    ws = isa.workspace(isa.sparse_workspace_size(None, aa, k))
+    out = torch.empty((B, Hq, 512), dtype=torch.float32, device=dev)
+    state = [hs, st, ss, hk]
+    for i in range(steps):
+        step = 20 + i
+        sel = np.full((B, k), -1, np.int32)
+        cand = np.full((B, m), -1, np.int32)
+        for b in range(B):
+            pick = np.sort(g.choice(n, size=int(g.integers(k // 2, k + 1)), replace=False))
+            sel[b, : pick.size] = pick
+            # candidates: some of the selection, some held tokens, new tokens
+            # (some past the valid length), in a random order, with padding
+            held = np.nonzero(state[0][b] >= 0)[0]
+            pool = np.unique(np.concatenate([
+                g.choice(pick, size=min(pick.size, m // 4), replace=False),
+                g.choice(held, size=min(held.size, m // 4), replace=False) if held.size else
+                np.array([], dtype=np.int64),
+                g.choice(n, size=m, replace=False)]))
+            c = g.permutation(pool)[: int(g.integers(m // 2, m + 1))]
+            cand[b, : c.size] = c
+            cand[b][g.random(m) < 0.05] = -1
+        sel_t = torch.from_numpy(sel).to(dev)
+        cand_t = torch.from_numpy(cand).to(dev)
+        isa.sparse_gather_attn_decode(aa, sel_t, 1, k, 1, out, None, ws)
+        isa.sparse_hot_update(None, aa, sel_t, k, 1, S, step, slot_token, slot_stamp, ws)
+        torch.cuda.synchronize()
+        state = _oracle_all(state[0], state[1], state[2], state[3], host_bits, sel, vl, step)
+        _check((hot_slot, slot_token, slot_stamp, hot_kv), state, f"update {step}")
+        isa.sparse_hot_prefetch(aa, cand_t, m, S, step, slot_token, slot_stamp)
+        torch.cuda.synchronize()
+        ref = [np.empty_like(x) for x in state]
+        for b in range(B):
+            r = hot_prefetch(state[0][b], state[1][b], state[2][b], state[3][b], host_bits[b],
+                             cand[b], vl[b], step)
+            for o, x in zip(ref, r):
+                o[b] = x
+        _check((hot_slot, slot_token, slot_stamp, hot_kv), ref, f"prefetch {step}")
+        state = ref
