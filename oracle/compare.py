@@ -52,16 +52,34 @@ def selection_ok(gpu_sel: np.ndarray, oracle_sel: np.ndarray,
 
 def scores_ok(gpu_scores: np.ndarray, oracle_scores: np.ndarray, k: int,
               valid: int) -> tuple[bool, float, float]:
-    """Scores within tau on every valid unit; returns (ok, max_err, tau)."""
+    """Scores within tau on every valid unit; returns (ok, max_err, tau).
+    A non-finite GPU score at a valid unit fails (error inf)."""
     _, tau = kth_tau(oracle_scores, k, valid)
     if valid == 0:
         return True, 0.0, tau
-    err = np.abs(gpu_scores[:valid].astype(np.float64) - oracle_scores[:valid])
+    g = np.asarray(gpu_scores[:valid], dtype=np.float64)
+    if not np.all(np.isfinite(g)):
+        return False, float("inf"), tau
+    err = np.abs(g - oracle_scores[:valid])
     m = float(err.max())
     return m <= tau, m, tau
 
 
 def attn_ok(gpu: np.ndarray, ref: np.ndarray, tol: float = ATTN_TOL):
-    err = np.abs(gpu.astype(np.float64) - ref)
-    m = float(np.nanmax(err)) if err.size else 0.0
+    """Max-abs difference of outputs (or lse values) within tol.
+
+    Non-finite entries must sit at the same positions with the same value on
+    both sides (an empty selection gives lse = -inf in the oracle); a NaN on
+    either side, or a shape mismatch, fails with error inf.  The maximum is
+    then taken over the finite entries."""
+    g = np.asarray(gpu, dtype=np.float64)
+    r = np.asarray(ref, dtype=np.float64)
+    if g.shape != r.shape or np.isnan(g).any() or np.isnan(r).any():
+        return False, float("inf")
+    gf, rf = np.isfinite(g), np.isfinite(r)
+    if not np.array_equal(gf, rf) or not np.array_equal(g[~gf], r[~rf]):
+        return False, float("inf")
+    if not gf.any():
+        return True, 0.0
+    m = float(np.abs(g[gf] - r[rf]).max())
     return m <= tol, m

@@ -148,8 +148,9 @@ def fathom_read_depth(q_bar: np.ndarray, var: np.ndarray, budget: int,
                       planes: int = 4) -> np.ndarray:
     """Per-channel read depth t_c in {0..planes} with sum_c t_c = budget.
 
-    [FA]: the query spends its bit budget by reverse water-filling over the
-    variance-weighted importance of its channels.  Written out:
+    [FA] abstract: each query divides its per-key bit budget among the
+    channels by reverse water-filling, with a channel's importance weighted
+    by its variance.  Written out:
       importance  imp_c = (q_bar_c * q_bar_c) * var_c
       the distortion of channel c read to depth t is modelled as
       imp_c * 4^-t, so reading plane j of channel c lowers it by

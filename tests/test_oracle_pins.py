@@ -181,7 +181,8 @@ def _fathom_data(n=300, D=7, seed=0):
 
 
 def test_prefix_of_planes_is_the_tbit_quantizer():
-    # "a prefix of t planes is exactly the channel's t-bit quantizer"
+    # Fathom abstract: reading the first t planes of a channel gives that
+    # channel's t-bit quantizer, exactly
     x, codes, zero, cell = _fathom_data()
     for t in range(5):
         q_t = O.fathom_tbit_quantize(x, zero[None], cell[None], t)
@@ -317,7 +318,8 @@ def test_fathom_full_depth_is_dequantised_dot_and_bits_agree():
 
 
 def test_fathom_full_budget_matches_exact_topk_of_dequantised_scores():
-    # "every per-token scan matches exact top-k decoding" at full depth
+    # Fathom abstract: a per-token scan agrees with exact top-k decoding; at
+    # full depth the plane scan is the 4-bit dequantised dot
     x, codes, zero, cell = _fathom_data(n=400, D=8, seed=9)
     qb = RNG.standard_normal(8)
     t = O.fathom_read_depth(qb, np.ones(8), 32)
