@@ -52,6 +52,17 @@ struct RowAddr {
 };
 
 
+// A row of zeros owned by the library, as wide as the widest row the
+// kernels read (a 576-element bf16 latent row, a 128-element fp32 row).
+// Masked positions (padding entries, tokens past seq_len, the prefetch pad
+// past a split's end) point here instead of at caller memory, so that the
+// zero probability they get multiplies finite zeros: 0 * NaN would turn a
+// whole head's output into NaN when the caller's row holds NaN or infinity
+// (an unfilled hot-buffer slot or an unused page).
+__device__ __attribute__((aligned(256))) uint16_t g_zero_row[576] = {0};
+
+__device__ __forceinline__ const char* zero_row() { return (const char*)g_zero_row; }
+
 // One halving step of a reduce-scatter over N partials: partner lanes
 // (given by xch) exchange halves; a lane with `up` keeps the upper half.
 template <int N, typename F>
@@ -146,8 +157,10 @@ __global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(AttnPlan p) {
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const int i = min(i0 + u, cnt - 1);
-      const int t = max(tok_s[i], 0);  // masked positions read token 0's row
-      kvs[u] = *(const f32x2*)((const float*)ra.k_row(b, kvh, t, 0, nullptr, 4) + 2 * lane);
+      const int t = tok_s[i];  // masked positions read the zero row
+      const float* kr = t >= 0 ? (const float*)ra.k_row(b, kvh, t, 0, nullptr, 4)
+                               : (const float*)zero_row();
+      kvs[u] = *(const f32x2*)(kr + 2 * lane);
     }
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
@@ -196,10 +209,11 @@ __global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(AttnPlan p) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
     for (int i = 0; i < cnt; ++i) {
-      // a masked position has probability 0; it reads token 0's row instead
-      const int t = max(tok_s[i], 0);
-      const float* vr = A.v_cache ? (const float*)ra.v_row(b, kvh, t, 4)
-                                  : (const float*)ra.k_row(b, kvh, t, 0, nullptr, 4);
+      // a masked position has probability 0 and reads the zero row
+      const int t = tok_s[i];
+      const float* vr = t < 0 ? (const float*)zero_row()
+                              : A.v_cache ? (const float*)ra.v_row(b, kvh, t, 4)
+                                          : (const float*)ra.k_row(b, kvh, t, 0, nullptr, 4);
       acc += *(const f32x4*)(vr + 4 * qd) * logit_s[h][i];
     }
     const float m = ml_s[h][0], l = ml_s[h][1];
@@ -317,11 +331,10 @@ __global__ __launch_bounds__(kMlaThreads, 1) void attn_mla_kernel(AttnPlan p) {
   RowAddr ra{A};
 
   // Row table: the K row address of every split position (masked positions
-  // and the prefetch pad point at a finite dummy row, so every load in the
-  // pipeline is unconditional) and, per 32-token tile, the valid-token bits.
-  const uint64_t dummy =
-      (uint64_t)(A.hot_slot ? (const char*)A.hot_kv + (int64_t)b * A.hot_stride_b * 2
-                            : (const char*)A.k_cache);
+  // and the prefetch pad point at the library's zero row, so every load in
+  // the pipeline is unconditional) and, per 32-token tile, the valid-token
+  // bits.
+  const uint64_t dummy = (uint64_t)zero_row();
   for (int base = 0; base < cnt; base += kMlaThreads) {
     const int i = base + tid;
     int t = -1;
@@ -625,9 +638,9 @@ __global__ __launch_bounds__(64 * kGqaWaves) void attn_gqa_kernel(AttnPlan p) {
     }
   }
 
-  // row table (K rows; masked positions point at a finite dummy row) and
-  // the valid-token bits of every tile
-  const uint64_t dummy = (uint64_t)(const char*)A.k_cache;
+  // row table (K rows; masked positions point at the library's zero row,
+  // for K and V alike) and the valid-token bits of every tile
+  const uint64_t dummy = (uint64_t)zero_row();
   for (int base = 0; base < ntiles * kTT; base += 64 * kGqaWaves) {
     const int i = base + tid;
     int t = -1;
@@ -649,8 +662,11 @@ __global__ __launch_bounds__(64 * kGqaWaves) void attn_gqa_kernel(AttnPlan p) {
       for (int s = 0; s < 4; ++s) T.k[mt][s] = *(gptr<const u32x4>)(kr + 64 * s);
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-      T.v[u] = *(gptr<const u32x4>)((const char*)rowp_s[tile * kTT + g + 4 * u] + vdelta + 16 * n);
+    for (int u = 0; u < 8; ++u) {
+      const uint64_t kp = rowp_s[tile * kTT + g + 4 * u];
+      const char* vp = kp == dummy ? (const char*)kp : (const char*)kp + vdelta;
+      T.v[u] = *(gptr<const u32x4>)(vp + 16 * n);
+    }
   };
 
   const float qk_scale = A.sm_scale * kLog2e;
