@@ -14,7 +14,7 @@
  *        HBM), Figure 1 caption (missing selected entries are fetched from
  *        host memory into HBM), the modelling paragraphs (2,048 selected
  *        entries per layer and step, a 4,096-token hot KV buffer per request)
- *        and the KV-lifecycle list ("fetch selected KV").
+ *        and the KV-lifecycle list (only the selected KV is fetched).
  *   [MM] "MiniMax-M3: share the sparse index top-k across layers and reuse
  *        the decode top-k buffer": description (a lightning-indexer pass
  *        picks the top-k KV blocks; the first layer of a group writes the
@@ -22,10 +22,10 @@
  *        no allocation, so graph capture never allocates; on ROCm a fixed
  *        tile configuration instead of runtime autotuning).
  *   [FA] "Fathom: Per-Query Read Depth for Sparse Decoding over Offloaded KV
- *        Caches": abstract (4-bit K stored channel-major as bit planes; a
- *        prefix of t planes is the channel's t-bit quantizer; each query
- *        spends its bit budget by reverse water-filling over the
- *        variance-weighted importance of its channels).
+ *        Caches": abstract (4-bit K stored channel-major as bit planes; the
+ *        first t planes of a channel form its t-bit quantizer; a query
+ *        divides its per-key bit budget among the channels by reverse
+ *        water-filling on variance-weighted channel importance).
  *
  * Conventions shared by every entry point
  *   - All pointers are device pointers owned by the caller unless stated.
@@ -185,15 +185,23 @@ int sparse_abi_version(void);
 const char* sparse_strerror(int status);
 const char* sparse_last_error(void);
 
-/* Bytes of workspace the calls below need.  Either args pointer may be NULL:
- * with only `ia`, enough for sparse_index_score + sparse_topk of those
- * scores; with only `aa`, enough for sparse_gather_attn_decode; with both,
- * enough for sparse_decode_step.  k is the number of selected units. */
+/* Bytes of workspace the calls below need.  [MM] description and ROCm
+ * note: the decode top-k buffer is allocated once per batch size and never
+ * inside a layer, so a captured graph never allocates; here every scratch
+ * byte of a step (scores, histogram parts, candidate lists, attention
+ * partials, miss staging) likewise lives in one caller-owned workspace,
+ * sized once by this call and reused by every step.  Either args pointer
+ * may be NULL: with only `ia`, enough for sparse_index_score +
+ * sparse_topk of those scores; with only `aa`, enough for
+ * sparse_gather_attn_decode; with both, enough for sparse_decode_step.  k is
+ * the number of selected units (k >= 1).  bytes: out, the size.  Errors: the
+ * argument checks of the matching entry points (nothing is launched). */
 int sparse_workspace_size(const sparse_index_args* ia,
                           const sparse_attn_args* aa, int32_t k,
                           size_t* bytes);
 
-/* Workspace for sparse_topk over `rows` rows of `n_units` scores. */
+/* Workspace for sparse_topk over `rows` rows of `n_units` scores (see
+ * sparse_workspace_size for why scratch is the caller's). */
 int sparse_topk_workspace_size(int32_t rows, int32_t n_units, int32_t k,
                                size_t* bytes);
 
@@ -207,26 +215,43 @@ int sparse_topk_workspace_size(int32_t rows, int32_t n_units, int32_t k,
 int sparse_read_depth(const sparse_index_args* ia, int8_t* depth_out,
                       void* stream);
 
-/* Step a2: index scores.  scores: [B][R][n_units] fp32 with R = 1 (DOT,
- * LIGHTNING) or R = Hkv (BITPLANE) and n_units = ceil(n / block_size).
- * Units at or past a request's valid length are written as -inf. */
+/* Step a2: index scores.  [XM] opening paragraph: the indexer scans the
+ * K-index that stays in HBM and scores every cached key against the current
+ * query; [MM] description: the lightning-indexer pass (and its reduction
+ * to KV blocks) runs in the first layer of a group; [FA] abstract: the
+ * per-token scan reads each channel's plane prefix (depths as for
+ * sparse_read_depth).  scores: [B][R][n_units] fp32, device, caller-owned,
+ * with R = 1 (DOT, LIGHTNING) or R = Hkv (BITPLANE) and n_units =
+ * ceil(n / block_size).  Units at or past a request's valid length are
+ * written as -inf.  ws: needed (sparse_workspace_size with only `ia`) for
+ * BITPLANE, which keeps the read depths and plane weights there; may be
+ * NULL for the other kinds.  Errors: EINVAL / EUNSUPPORTED from the
+ * argument checks, EWORKSPACE, EHIP. */
 int sparse_index_score(const sparse_index_args* ia, float* scores, void* ws,
                        size_t ws_bytes, void* stream);
 
-/* Step a3: exact top-k of each score row.  Row r starts at
- * scores + r*row_stride and has n_units entries of which the first
- * valid_units[r / rows_per_valid] are valid (valid_units NULL = all).
- * Ties go to the lower index.  idx_out: [rows][k] int32, the selected unit
- * indices in ascending order, -1-padded when fewer than k are valid.
- * val_out (nullable): [rows][k] their scores (-inf for padding).
- * Scores must not be NaN. */
+/* Step a3: exact top-k of each score row.  [MM] description: the top-k
+ * KV blocks are written into a persistent int32 buffer that later layers
+ * read; [XM] modelling paragraphs: 2,048 entries per layer and step.  Row r
+ * starts at scores + r*row_stride (device fp32) and has n_units entries of
+ * which the first valid_units[r / rows_per_valid] are valid (valid_units
+ * NULL = all; rows_per_valid lets the rows of one request -- e.g. its KV
+ * heads -- share one length entry).  Ties go to the lower index.  idx_out:
+ * [rows][k] int32, the selected unit indices in ascending order, -1-padded
+ * when fewer than k are valid.  val_out (nullable): [rows][k] their scores
+ * (-inf for padding).  Scores must not be NaN.  ws: sparse_topk_workspace_
+ * size bytes.  Errors: EINVAL (sizes, NULL outputs), EUNSUPPORTED
+ * (n_units above 4194304), EWORKSPACE, EHIP. */
 int sparse_topk(const float* scores, int32_t rows, int32_t n_units,
                 int64_t row_stride, const int32_t* valid_units,
                 int32_t rows_per_valid, int32_t k, int32_t* idx_out,
                 float* val_out, void* ws, size_t ws_bytes, void* stream);
 
 /* Step a6 (with a4, and a5 when aa->hot_slot is set): attention of each
- * query head over the selected units.  sel: [B][sel_heads][k] int32 unit
+ * query head over the selected units ([XM] opening paragraph: a step reads
+ * only the selected KV entries; Figure 1 caption: selected entries missing
+ * from the hot buffer are fetched from host memory).  Padding entries and
+ * tokens past seq_len read no caller memory.  sel: [B][sel_heads][k] int32 unit
  * ids (-1 = padding), sel_heads = 1 (shared by all KV heads) or Hkv (query
  * head h uses row h / (Hq/Hkv)).  sel_unit = 1 (tokens) or 64 (a unit u is
  * tokens 64u .. 64u+63; tokens past seq_len are skipped).

@@ -9,7 +9,6 @@ fails to load, every call raises.
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 
 import torch
@@ -209,9 +208,9 @@ def bitplane_index_args(q: torch.Tensor, planes: torch.Tensor,
 
 
 def attn_args(q: torch.Tensor, k_cache: torch.Tensor | None,
-              v_cache: torch.Tensor | None = None, *, n: int,
+              v_cache: torch.Tensor | None = None, *, n: int, d_v: int,
+              sm_scale: float,
               page_table: torch.Tensor | None = None, page_size: int = 0,
-              sm_scale: float | None = None,
               seq_lens: torch.Tensor | None = None,
               hot_slot: torch.Tensor | None = None,
               hot_kv: torch.Tensor | None = None,
@@ -222,25 +221,26 @@ def attn_args(q: torch.Tensor, k_cache: torch.Tensor | None,
     caches, or (latent, v_cache None) [B][n][d_qk], or with a page table a
     pool [pages][page_size][d_qk] (or [pages][page_size][Hkv][d]).  Hot
     buffer: hot_slot [B][n] int32, hot_kv [B][slots][d_qk], host_kv pinned
-    [B][n][d_qk] (its device alias is looked up here)."""
+    [B][n][d_qk] (its device alias is looked up here).  d_v (the value
+    width; latent rows use their first d_v elements as the value) and
+    sm_scale (the softmax scale) are the caller's: nothing is inferred."""
     a = AttnArgs()
     B, Hq, dqk = q.shape
     a.batch, a.n, a.seq_lens = B, n, _p(seq_lens)
-    a.n_q_heads, a.d_qk = Hq, dqk
+    a.n_q_heads, a.d_qk, a.d_v = Hq, dqk, d_v
+    a.sm_scale = sm_scale
     a.dtype = _DT[q.dtype]
     a.q, a.q_stride_b, a.q_stride_h = _p(q), q.stride(0), q.stride(1)
     refs = [q, k_cache, v_cache, page_table, seq_lens, hot_slot, hot_kv, host_kv]
     latent = v_cache is None
     if hot_slot is not None:
         a.n_kv_heads = 1
-        a.d_v = 512 if dqk == 576 else dqk
         a.hot_slot, a.hs_stride_b = _p(hot_slot), hot_slot.stride(0)
         a.hot_kv, a.hot_stride_b, a.hot_stride_s = _p(hot_kv), hot_kv.stride(0), hot_kv.stride(1)
         dev = host_device_pointer(host_kv)
         a.host_kv, a.host_stride_b, a.host_stride_t = dev, host_kv.stride(0), host_kv.stride(1)
     elif latent:
         a.n_kv_heads = 1
-        a.d_v = 512 if dqk == 576 else dqk
         a.k_cache = _p(k_cache)
         if page_table is not None:
             a.kv_stride_t = k_cache.stride(-2)
@@ -248,7 +248,8 @@ def attn_args(q: torch.Tensor, k_cache: torch.Tensor | None,
             a.kv_stride_b, a.kv_stride_t = k_cache.stride(0), k_cache.stride(1)
     else:
         a.n_kv_heads = k_cache.shape[-2]
-        a.d_v = v_cache.shape[-1]
+        if v_cache.shape[-1] != d_v:
+            raise ValueError(f"v_cache rows hold {v_cache.shape[-1]} values, d_v is {d_v}")
         if v_cache.stride() != k_cache.stride():
             raise ValueError("k_cache and v_cache must share strides")
         a.k_cache, a.v_cache = _p(k_cache), _p(v_cache)
@@ -260,7 +261,6 @@ def attn_args(q: torch.Tensor, k_cache: torch.Tensor | None,
     if page_table is not None:
         a.page_table, a.pt_stride_b, a.page_size = (
             _p(page_table), page_table.stride(0), page_size)
-    a.sm_scale = sm_scale if sm_scale is not None else 1.0 / math.sqrt(dqk)
     return _Holder(a, *refs)
 
 

@@ -12,8 +12,6 @@ layer.  It allocates nothing inside ``run()``.
 """
 from __future__ import annotations
 
-import math
-
 import torch
 
 from . import (attn_args, bitplane_index_args, dot_index_args,
@@ -35,30 +33,32 @@ class StepRunner:
             keys = inp["k_cache"][:, :, 0, :]
             self.ia = dot_index_args(inp["q"], keys, 1, seq)
             self.layer_args.append((attn_args(inp["q"], inp["k_cache"], inp["v_cache"],
-                                              n=n, seq_lens=seq), inp["q"].shape[1]))
+                                              n=n, d_v=w.d_v, sm_scale=w.sm_scale,
+                                              seq_lens=seq), inp["q"].shape[1]))
             self.unit, self.rows = 1, 1
         elif w.kind == "lightning":
             self.ia = lightning_index_args(inp["q_idx"], inp["head_w"], inp["k8"],
                                            inp["k_scale"], seq)
             if hot is not None:
-                aa = attn_args(inp["q"], None, n=n, seq_lens=seq,
-                               sm_scale=1.0 / math.sqrt(w.d_qk),
+                aa = attn_args(inp["q"], None, n=n, d_v=w.d_v, sm_scale=w.sm_scale,
+                               seq_lens=seq,
                                hot_slot=hot["hot_slot"], hot_kv=hot["hot_kv"],
                                host_kv=hot["host_kv"])
             elif "kv_pool" in inp:
-                aa = attn_args(inp["q"], inp["kv_pool"], n=n, seq_lens=seq,
-                               page_table=inp["page_table"], page_size=w.page,
-                               sm_scale=1.0 / math.sqrt(w.d_qk))
+                aa = attn_args(inp["q"], inp["kv_pool"], n=n, d_v=w.d_v,
+                               sm_scale=w.sm_scale, seq_lens=seq,
+                               page_table=inp["page_table"], page_size=w.page)
             else:
-                aa = attn_args(inp["q"], inp["kv"], n=n, seq_lens=seq,
-                               sm_scale=1.0 / math.sqrt(w.d_qk))
+                aa = attn_args(inp["q"], inp["kv"], n=n, d_v=w.d_v, sm_scale=w.sm_scale,
+                               seq_lens=seq)
             self.layer_args.append((aa, w.hq))
             self.unit, self.rows = 1, 1
         elif w.kind == "block":
             self.ia = dot_index_args(inp["q_idx"], inp["k_idx"], w.block, seq)
             for layer in inp["layers"]:
                 self.layer_args.append((attn_args(layer["q"], layer["k_cache"],
-                                                  layer["v_cache"], n=n, seq_lens=seq),
+                                                  layer["v_cache"], n=n, d_v=w.d_v,
+                                                  sm_scale=w.sm_scale, seq_lens=seq),
                                         w.hq))
             self.unit, self.rows = w.block, 1
         elif w.kind == "fathom":
@@ -66,7 +66,8 @@ class StepRunner:
                                           inp["chan_scale"], inp["chan_var"], w.budget,
                                           n, seq, depth_in=inp.get("depth_in"))
             self.layer_args.append((attn_args(inp["q"], inp["k_cache"], inp["v_cache"],
-                                              n=n, seq_lens=seq), w.hq))
+                                              n=n, d_v=w.d_v, sm_scale=w.sm_scale,
+                                              seq_lens=seq), w.hq))
             self.unit, self.rows = 1, w.hkv
         else:
             raise ValueError(w.kind)

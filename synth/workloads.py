@@ -10,6 +10,7 @@ several tiles and end in ragged tails.
 """
 from __future__ import annotations
 
+import math
 from dataclasses import dataclass, field, replace
 
 
@@ -40,6 +41,13 @@ class Workload:
     @property
     def mla(self) -> bool:
         return self.kind == "lightning"
+
+    @property
+    def sm_scale(self) -> float:
+        """The softmax scale of the workload's attention: 1/sqrt(d_qk) (the
+        fp32 workload states 1/sqrt(128); the latent workloads take the
+        same rule over the 576-wide query/key rows)."""
+        return 1.0 / math.sqrt(self.d_qk)
 
     @property
     def n_units(self) -> int:

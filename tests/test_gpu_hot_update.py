@@ -90,7 +90,7 @@ def test_hot_update_sequence_matches_oracle(B, n, S, k, steps, valid):
     hot_kv = torch.from_numpy(hk.view(np.int16)).to(dev).view(torch.bfloat16)
     q = torch.from_numpy(g.normal(size=(B, Hq, d)).astype(np.float32) * 0.1).to(torch.bfloat16).to(dev)
     seq = torch.from_numpy(vl.astype(np.int32)).to(dev)
-    aa = isa.attn_args(q, None, n=n, seq_lens=seq, sm_scale=d ** -0.5,
+    aa = isa.attn_args(q, None, n=n, d_v=512, sm_scale=d ** -0.5, seq_lens=seq,
                        hot_slot=hot_slot, hot_kv=hot_kv, host_kv=host)
     ws = isa.workspace(isa.sparse_workspace_size(None, aa, k))
     out = torch.empty((B, Hq, 512), dtype=torch.float32, device=dev)
@@ -140,7 +140,7 @@ def test_hot_update_block_units():
     hot_kv = torch.from_numpy(hk.view(np.int16)).to(dev).view(torch.bfloat16)
     q = torch.from_numpy(g.normal(size=(B, Hq, d)).astype(np.float32) * 0.1).to(torch.bfloat16).to(dev)
     seq = torch.from_numpy(vl.astype(np.int32)).to(dev)
-    aa = isa.attn_args(q, None, n=n, seq_lens=seq, sm_scale=d ** -0.5,
+    aa = isa.attn_args(q, None, n=n, d_v=512, sm_scale=d ** -0.5, seq_lens=seq,
                        hot_slot=hot_slot, hot_kv=hot_kv, host_kv=host)
     ws = isa.workspace(isa.sparse_workspace_size(None, aa, kb * unit))
     out = torch.empty((B, Hq, 512), dtype=torch.float32, device=dev)
@@ -241,7 +241,7 @@ def test_hot_prefetch_matches_oracle(B, n, S, k, m, steps, valid):
     hot_kv = torch.from_numpy(hk.view(np.int16)).to(dev).view(torch.bfloat16)
     q = torch.from_numpy(g.normal(size=(B, Hq, d)).astype(np.float32) * 0.1).to(torch.bfloat16).to(dev)
     seq = torch.from_numpy(vl.astype(np.int32)).to(dev)
-    aa = isa.attn_args(q, None, n=n, seq_lens=seq, sm_scale=d ** -0.5,
+    aa = isa.attn_args(q, None, n=n, d_v=512, sm_scale=d ** -0.5, seq_lens=seq,
                        hot_slot=hot_slot, hot_kv=hot_kv, host_kv=host)
     ws = isa.workspace(isa.sparse_workspace_size(None, aa, k))
     out = torch.empty((B, Hq, 512), dtype=torch.float32, device=dev)

@@ -19,11 +19,16 @@ from oracle import oracle as O
 pytestmark = pytest.mark.gpu
 
 CASES = [
-    # (B, n, Hq, k, paged, valid lengths or None)
-    (2, 3000, 64, 500, False, [3000, 1700]),
-    (1, 6000, 192, 2048, True, None),
-    (3, 4096, 256, 96, True, [4096, 4000, 100]),
-    (1, 2500, 128, 64, False, None),      # few tokens: one split
+    # (B, n, Hq, k, paged, valid lengths or None, q scale)
+    (2, 3000, 64, 500, False, [3000, 1700], 0.3),
+    (1, 6000, 192, 2048, True, None, 0.3),
+    (3, 4096, 256, 96, True, [4096, 4000, 100], 0.3),
+    (1, 2500, 128, 64, False, None, 0.3),      # few tokens: one split
+    # a peaked softmax at k = 2048: the logits of every head span more than
+    # 8, so the few rows of largest weight decide the output and a wrong or
+    # missing row moves it far beyond the bar
+    (2, 8192, 128, 2048, True, None, 3.0),
+    (1, 5000, 64, 2048, False, [4500], 4.0),
 ]
 
 
@@ -31,12 +36,13 @@ def _bits(t):
     return t.view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-@pytest.mark.parametrize("B,n,Hq,k,paged,valid", CASES,
-                         ids=[f"H{c[2]}-k{c[3]}-{'paged' if c[4] else 'flat'}" for c in CASES])
-def test_mla_attention_matches_oracle(B, n, Hq, k, paged, valid):
-    print(f"[mla] B={B} n={n} Hq={Hq} k={k} paged={paged}", flush=True)
+@pytest.mark.parametrize("B,n,Hq,k,paged,valid,qs", CASES,
+                         ids=[f"H{c[2]}-k{c[3]}-{'paged' if c[4] else 'flat'}-q{c[6]}"
+                              for c in CASES])
+def test_mla_attention_matches_oracle(B, n, Hq, k, paged, valid, qs):
+    print(f"[mla] B={B} n={n} Hq={Hq} k={k} paged={paged} q scale {qs}", flush=True)
     g = np.random.default_rng(n + Hq + k)
-    q = torch.from_numpy(g.normal(size=(B, Hq, 576)).astype(np.float32) * 0.3).to(torch.bfloat16).cuda()
+    q = torch.from_numpy(g.normal(size=(B, Hq, 576)).astype(np.float32) * qs).to(torch.bfloat16).cuda()
     rows = g.normal(size=(B, n, 576)).astype(np.float32)
     if paged:
         page = 64
@@ -59,7 +65,8 @@ def test_mla_attention_matches_oracle(B, n, Hq, k, paged, valid):
         row[g.choice(k, size=max(1, k // 40), replace=False)] = -1
         sel[b] = row
     seq = None if valid is None else torch.tensor(valid, dtype=torch.int32, device="cuda")
-    aa = isa.attn_args(q, kc, None, n=n, page_table=pt, page_size=64 if paged else 0,
+    aa = isa.attn_args(q, kc, None, n=n, d_v=512, sm_scale=576 ** -0.5, page_table=pt,
+                       page_size=64 if paged else 0,
                        seq_lens=seq)
     out = torch.empty((B, Hq, 512), dtype=torch.float32, device="cuda")
     lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
@@ -75,6 +82,9 @@ def test_mla_attention_matches_oracle(B, n, Hq, k, paged, valid):
         toks = O.expand_selection(sel[b], 1, v)
         keys = O.decode_bf16(R[b, toks])
         ro, rl = O.attention(qn[b], keys, keys[:, :512], scale)
+        if qs >= 3.0:
+            logits = scale * qn[b] @ keys.T
+            assert np.all(logits.max(1) - logits.min(1) > 8.0)
         ok, err = C.attn_ok(go[b], ro)
         assert ok, (b, err)
         ok, err = C.attn_ok(gl[b], rl)
