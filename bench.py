@@ -61,6 +61,13 @@ def algorithmic_bytes(w, bits=None) -> dict:
     return out
 
 
+def compute_dtype(w) -> str:
+    """The arithmetic type of the step's contractions: fp32 for the fp32
+    workload; otherwise bf16 MFMA with fp32 accumulation (the fp8 K-index
+    and the 4-bit planes are widened exactly before they are used)."""
+    return "f32" if w.dtype == "f32" else "bf16"
+
+
 def score_kernel_bytes(w, bits=None) -> int:
     """Algorithmic bytes of one launch of the index-scan kernel."""
     bits = w.budget if bits is None else bits
@@ -259,14 +266,24 @@ def main() -> int:
     torch.cuda.synchronize()
 
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    # HIP events on the stream the steps run on bracket exactly the K timed
+    # steps, inside a synchronize on both sides; the host clock around the
+    # same region is reported beside it (it adds the fixed cost of starting
+    # and draining the queue, which a short run does not amortise)
+    t_beg = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
+    t_beg.record(stream)
     for i in range(args.steps):
         if graphs:
             graphs[i % ns].replay()
         else:
             sets[i % ns][1].run()
+    t_end.record(stream)
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    wall = time.perf_counter() - t0
+    elapsed = t_beg.elapsed_time(t_end) * 1e-3
     ms = 1e3 * elapsed / args.steps
     steps_s = args.steps / elapsed
 
@@ -305,7 +322,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": compute_dtype(w),
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.B, "context": w.n, "top_k": w.k,
                    "index_heads": w.idx_heads, "attn_heads": w.hq, "kv_heads": w.hkv,
@@ -314,6 +331,7 @@ def main() -> int:
                    "miss_rate": miss_rate if w.hot else None,
                    "fixed_depth_bits": bits, "host_planes": bool(args.host_planes and w.kind == "fathom"),
                    "graph": not args.no_graph},
+        "host_wall_ms_per_step": round(1e3 * wall / args.steps, 5),
         "step_bytes": ab["total"],
         "step_GBps": round(ab["total"] / (ms * 1e-3) / 1e9, 1),
         "step_hbm_frac": round(ab["total"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -475,7 +493,7 @@ def run_policy(args) -> int:
         "value": round(args.steps / elapsed, 2), "unit": "steps/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(1e3 * elapsed / args.steps, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None, "dtype": compute_dtype(w), "data": "synthetic",
         "config": {"workload": w.name, "batch": w.B, "context": w.n, "top_k": w.k,
                    "hot_tokens": S, "policy": args.policy, "drift": args.drift,
                    "start_miss_rate": w.miss_rate, "prefetch": M, "graph": False},
