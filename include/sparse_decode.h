@@ -273,6 +273,26 @@ int sparse_decode_step(const sparse_index_args* ia, const sparse_attn_args* aa,
                        int32_t k, int32_t* topk_out, float* out, float* lse,
                        void* ws, size_t ws_bytes, void* stream);
 
+/* sparse_decode_step without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation.  The step's scratch lives in a
+ * fixed device array of the library, SPARSE_NOALLOC_SCRATCH_BYTES (128 MiB)
+ * per device, which each GPU the library runs on holds from its first use
+ * until the process ends; nothing is allocated or freed by the call.  A step
+ * whose sparse_workspace_size exceeds that returns SPARSE_EWORKSPACE before
+ * anything is launched (at 128K context this covers batch 32 of the
+ * lightning indexer, not the hot-buffer batches of 109 or 241).  Every call
+ * on one GPU shares that GPU's array: calls that overlap on one GPU (two
+ * streams, or two host threads) race and must be ordered by the caller.
+ * The first call on each device looks the array's address up and should be
+ * made outside graph capture.  Arguments, outputs and errors otherwise as
+ * for sparse_decode_step. */
+#define SPARSE_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+int sparse_decode_step_noalloc(const sparse_index_args* ia,
+                               const sparse_attn_args* aa, int32_t k,
+                               int32_t* topk_out, float* out, float* lse,
+                               void* stream);
+
 /* Decode-side append: after a step, the new token of each request joins
  * the history the next step reads -- [XM] KV-lifecycle list (generated KV
  * is appended to the history), [MM] the decode path's sparse-KV store (the

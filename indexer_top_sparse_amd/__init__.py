@@ -89,6 +89,8 @@ def lib() -> ctypes.CDLL:
                                                 _vp, _vp, _vp, ctypes.c_size_t, _vp]
         L.sparse_decode_step.argtypes = [P(IndexArgs), P(AttnArgs), _i32, _vp, _vp,
                                          _vp, _vp, ctypes.c_size_t, _vp]
+        L.sparse_decode_step_noalloc.argtypes = [P(IndexArgs), P(AttnArgs), _i32, _vp, _vp,
+                                                 _vp, _vp]
         L.sparse_host_device_pointer.argtypes = [_vp, P(_vp)]
         L.sparse_append_token.argtypes = [P(IndexArgs), P(AttnArgs), _vp, _vp, _vp, _vp, _vp]
         L.sparse_hot_update.argtypes = [P(IndexArgs), P(AttnArgs), _vp, _i32, _i32, _i32,
@@ -97,6 +99,7 @@ def lib() -> ctypes.CDLL:
         for f in ("sparse_workspace_size", "sparse_topk_workspace_size",
                   "sparse_read_depth", "sparse_index_score", "sparse_topk",
                   "sparse_gather_attn_decode", "sparse_decode_step",
+                  "sparse_decode_step_noalloc",
                   "sparse_host_device_pointer", "sparse_append_token", "sparse_hot_update",
                   "sparse_hot_prefetch"):
             getattr(L, f).restype = ctypes.c_int
@@ -323,6 +326,15 @@ def sparse_decode_step(ia: _Holder, aa: _Holder, k: int, topk_out: torch.Tensor,
                        ws: torch.Tensor, stream=None) -> None:
     _check(lib().sparse_decode_step(ia.ref(), aa.ref(), k, _p(topk_out), _p(out),
                                     _p(lse), _p(ws), ws.numel(), _stream(stream)))
+
+
+def sparse_decode_step_noalloc(ia: _Holder, aa: _Holder, k: int, topk_out: torch.Tensor,
+                               out: torch.Tensor, lse: torch.Tensor | None,
+                               stream=None) -> None:
+    """sparse_decode_step with its scratch in the library's fixed device
+    array instead of a caller workspace (no allocation anywhere)."""
+    _check(lib().sparse_decode_step_noalloc(ia.ref(), aa.ref(), k, _p(topk_out), _p(out),
+                                            _p(lse), _stream(stream)))
 
 
 def sparse_append_token(ia: _Holder | None, aa: _Holder | None, pos: torch.Tensor,

@@ -1,13 +1,22 @@
 // extern "C" entry points: argument validation, workspace layout, dispatch.
 // No entry point allocates, frees or synchronises; all scratch lives in the
-// caller's workspace and all work goes on the caller's stream.
+// caller's workspace (sparse_decode_step_noalloc: in a fixed device array)
+// and all work goes on the caller's stream.
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "common.hpp"
+
+// Scratch of sparse_decode_step_noalloc: device memory of this code object,
+// held by every GPU the library runs on until the process ends.  Its name
+// is a host-side stand-in in host code: host code uses only the device
+// address hipGetSymbolAddress returns for the current device.
+static constexpr size_t kNoAllocScratchBytes = SPARSE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
 
 namespace {
 
@@ -40,6 +49,12 @@ int64_t esize(int dt) { return dt == SPARSE_F32 ? 4 : (dt == SPARSE_BF16 ? 2 : 1
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Device address of `scratch` on each device, looked up once per device
+// with that device current.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
 
 // ------------------------------------------------------------------ layout
 struct IndexLayout {
@@ -357,6 +372,28 @@ int run_attn(const sparse_attn_args& a, const int32_t* sel, int sel_heads, int k
   return SPARSE_OK;
 }
 
+// Argument checks of the fused step (before anything is launched) and the
+// workspace it needs.
+int check_step(const sparse_index_args* ia, const sparse_attn_args* aa, int32_t k,
+               const int32_t* topk_out, const float* out, size_t* need) {
+  int rc = check_index(ia);
+  if (rc) return rc;
+  const bool bitplane = ia->kind == SPARSE_SCORE_BITPLANE;
+  const int sel_heads = bitplane ? ia->n_kv_heads : 1;
+  const int unit = ia->kind == SPARSE_SCORE_DOT ? ia->block_size : 1;
+  rc = check_attn(aa, sel_heads, k, unit);
+  if (rc) return rc;
+  CHECK(ia->batch == aa->batch, SPARSE_EINVAL, "index batch %d != attention batch %d",
+        ia->batch, aa->batch);
+  CHECK(ia->n <= aa->n, SPARSE_EINVAL, "index n %d > attention n %d", ia->n, aa->n);
+  if (bitplane)
+    CHECK(ia->n_kv_heads == aa->n_kv_heads, SPARSE_EINVAL, "KV heads differ");
+  *need = 0;
+  if (ia->batch == 0) return SPARSE_OK;
+  CHECK(topk_out && out, SPARSE_EINVAL, "topk_out / out NULL");
+  return sparse_workspace_size(ia, aa, k, need);
+}
+
 }  // namespace
 
 extern "C" {
@@ -479,24 +516,14 @@ int sparse_gather_attn_decode(const sparse_attn_args* aa, const int32_t* sel,
 int sparse_decode_step(const sparse_index_args* ia, const sparse_attn_args* aa, int32_t k,
                        int32_t* topk_out, float* out, float* lse, void* ws,
                        size_t ws_bytes, void* stream) {
-  int rc = check_index(ia);
+  size_t need = 0;
+  int rc = check_step(ia, aa, k, topk_out, out, &need);
   if (rc) return rc;
+  if (ia->batch == 0) return SPARSE_OK;
+  CHECK(ws && ws_bytes >= need, SPARSE_EWORKSPACE, "workspace %zu < %zu", ws_bytes, need);
   const bool bitplane = ia->kind == SPARSE_SCORE_BITPLANE;
   const int sel_heads = bitplane ? ia->n_kv_heads : 1;
   const int unit = ia->kind == SPARSE_SCORE_DOT ? ia->block_size : 1;
-  rc = check_attn(aa, sel_heads, k, unit);
-  if (rc) return rc;
-  CHECK(ia->batch == aa->batch, SPARSE_EINVAL, "index batch %d != attention batch %d",
-        ia->batch, aa->batch);
-  CHECK(ia->n <= aa->n, SPARSE_EINVAL, "index n %d > attention n %d", ia->n, aa->n);
-  if (bitplane)
-    CHECK(ia->n_kv_heads == aa->n_kv_heads, SPARSE_EINVAL, "KV heads differ");
-  if (ia->batch == 0) return SPARSE_OK;
-  CHECK(topk_out && out, SPARSE_EINVAL, "topk_out / out NULL");
-  size_t need = 0;
-  rc = sparse_workspace_size(ia, aa, k, &need);
-  if (rc) return rc;
-  CHECK(ws && ws_bytes >= need, SPARSE_EWORKSPACE, "workspace %zu < %zu", ws_bytes, need);
   hipStream_t s = (hipStream_t)stream;
   char* w = (char*)ws;
   IndexLayout L = index_layout(*ia, true);
@@ -511,6 +538,36 @@ int sparse_decode_step(const sparse_index_args* ia, const sparse_attn_args* aa, 
   rc = run_topk(tp, true, s);
   if (rc) return rc;
   return run_attn(*aa, topk_out, sel_heads, k, unit, out, lse, w, L.end, s);
+}
+
+int sparse_decode_step_noalloc(const sparse_index_args* ia, const sparse_attn_args* aa,
+                               int32_t k, int32_t* topk_out, float* out, float* lse,
+                               void* stream) {
+  size_t need = 0;
+  int rc = check_step(ia, aa, k, topk_out, out, &need);
+  if (rc) return rc;
+  if (ia->batch == 0) return SPARSE_OK;
+  CHECK(need <= kNoAllocScratchBytes, SPARSE_EWORKSPACE,
+        "this step needs %zu bytes of scratch, above the %zu bytes the no-allocation "
+        "entry point holds per device; use sparse_decode_step with a workspace",
+        need, kNoAllocScratchBytes);
+  int dev = 0;
+  HIPCHECK(hipGetDevice(&dev));
+  CHECK(dev >= 0 && dev < kMaxDevices, SPARSE_EUNSUPPORTED, "device %d above %d", dev,
+        kMaxDevices - 1);
+  void* ptr = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+      void* p = nullptr;
+      HIPCHECK(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+      CHECK(p != nullptr, SPARSE_EHIP, "no device address for the scratch array");
+      g_scratch_ptr[dev] = p;
+    }
+    ptr = g_scratch_ptr[dev];
+  }
+  return sparse_decode_step(ia, aa, k, topk_out, out, lse, ptr, kNoAllocScratchBytes,
+                            stream);
 }
 
 int sparse_append_token(const sparse_index_args* ia, const sparse_attn_args* aa,

@@ -258,3 +258,24 @@ def test_hot_prefetch_validation_codes():
     assert f(ctypes.byref(b), FAKE, 16, 64, 3, FAKE, FAKE, None) == isa.SPARSE_EINVAL
     # an empty batch is a no-op
     assert f(ctypes.byref(_hot_attn(B=0)), FAKE, 16, 64, 3, FAKE, FAKE, None) == isa.SPARSE_OK
+
+
+def test_decode_step_noalloc_checks_before_any_device_call():
+    L = isa.lib()
+    # above the fixed scratch: 32 requests at 1M tokens need far more than 128 MiB
+    ia, aa = _lightning(B=32, n=1 << 20), _mla_attn(B=32, n=1 << 20)
+    rc = L.sparse_decode_step_noalloc(ctypes.byref(ia), ctypes.byref(aa), 2048, FAKE, FAKE,
+                                      None, None)
+    assert rc == isa.SPARSE_EWORKSPACE
+    assert b"no-allocation" in L.sparse_last_error()
+    # the same argument checks as sparse_decode_step
+    ia, aa = _lightning(B=2), _mla_attn(B=3)
+    assert L.sparse_decode_step_noalloc(ctypes.byref(ia), ctypes.byref(aa), 16, FAKE, FAKE,
+                                        None, None) == isa.SPARSE_EINVAL
+    ia, aa = _lightning(B=2), _mla_attn(B=2)
+    assert L.sparse_decode_step_noalloc(ctypes.byref(ia), ctypes.byref(aa), 16, None, FAKE,
+                                        None, None) == isa.SPARSE_EINVAL
+    # an empty batch is a valid no-op
+    ia, aa = _lightning(B=0), _mla_attn(B=0)
+    assert L.sparse_decode_step_noalloc(ctypes.byref(ia), ctypes.byref(aa), 16, None, None,
+                                        None, None) == isa.SPARSE_OK

@@ -1,0 +1,46 @@
+"""GPU: the no-allocation step (sparse_decode_step_noalloc) against the step
+with a caller workspace (sparse_decode_step), called through the C ABI.
+
+Two calls in a row on the fixed scratch, the second with a smaller input, so
+that the second runs on scratch the first has filled; each must give the
+same selection, outputs and log-sum-exp as the workspace step, bit for bit
+(both run the same kernels in the same order), and the first call's input
+is run once more at the end.  The workloads are the lightning indexer
+(paged latent rows) and the Fathom scan (per-KV-head selections).
+"""
+import pytest
+import torch
+
+import indexer_top_sparse_amd as isa
+from indexer_top_sparse_amd.runner import StepRunner
+import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def _both(w):
+    print(f"[noalloc] {w.name} B={w.B} n={w.n} k={w.k}", flush=True)
+    inp = synth.make_inputs(w, "cuda")
+    r = StepRunner(inp)
+    r.run()
+    aa = r.layer_args[0][0]
+    topk = torch.full_like(r.topk, -7)
+    out = torch.full_like(r.outs[0], float("nan"))
+    lse = torch.full_like(r.lses[0], float("nan"))
+    isa.sparse_decode_step_noalloc(r.ia, aa, w.k, topk, out, lse)
+    torch.cuda.synchronize()
+    assert torch.equal(topk, r.topk)
+    assert torch.equal(out, r.outs[0])
+    assert torch.equal(lse, r.lses[0])
+
+
+@pytest.mark.parametrize("kind", ["lightning", "fathom"])
+def test_noalloc_matches_workspace_step(kind):
+    big = synth.get(f"{kind}_small")
+    small = big.with_(B=big.B - 1, n=big.n // 2, k=big.k // 2,
+                      seq_lens=tuple(min(v, big.n // 2) - 7 * i
+                                     for i, v in enumerate(big.seq_lens[:big.B - 1])),
+                      seed=big.seed + 1)
+    _both(big)
+    _both(small)
+    _both(big)
