@@ -431,6 +431,9 @@ def run_policy(args) -> int:
         qs.append(q.clone())
     misses = torch.zeros((), dtype=torch.int64, device=dev)
     selected = torch.zeros((), dtype=torch.int64, device=dev)
+    # missed rows of every step (warm-up included, in dispatch order), so that
+    # a kernel trace's miss-fetch durations pair with the bytes each moved
+    miss_log = torch.zeros(total, dtype=torch.int64, device=dev)
     seq = inp.get("seq_lens")
     vl = (seq if seq is not None else torch.full((w.B,), w.n, device=dev)).view(-1, 1)
     upd = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -458,7 +461,8 @@ def run_policy(args) -> int:
         sel = r.topk[:, 0]
         ok = (sel >= 0) & (sel < vl)
         hit = torch.gather(hs, 1, sel.clamp(min=0).long()) >= 0
-        misses.add_((ok & ~hit).sum())
+        miss_log[i] = (ok & ~hit).sum()
+        misses.add_(miss_log[i])
         selected.add_(ok.sum())
         if timed:
             upd[i - args.warmup][0].record()
@@ -501,6 +505,8 @@ def run_policy(args) -> int:
                    "hot_tokens": S, "policy": args.policy, "drift": args.drift,
                    "start_miss_rate": w.miss_rate, "prefetch": M, "graph": False},
         "measured_miss_rate": round(misses.item() / max(selected.item(), 1), 4),
+        "miss_rows_per_step": miss_log.cpu().tolist(),
+        "row_bytes": w.d_qk * 2,
         "update_us_per_call": round(upd_us, 2),
         "prefetch_us_per_call": round(pf_us, 2) if M else None,
     }

@@ -13,6 +13,8 @@ a step, against the oracle (oracle/hot.py), bit for bit.
   than free slots.
 * The fused step (sparse_decode_step, lightning indexer) on the small
   hot-buffer workload, then the update with the step's own selection.
+* The buffer and selection sizes of the hot-buffer workloads (4096 slots,
+  2048 selected tokens, 2048 prefetch candidates), beside small ones.
 * The prefetch (sparse_hot_prefetch) after each update of a sequence:
   candidate lists that mix resident tokens, new tokens, padding and tokens
   past the valid length, more candidates than free slots, against the
@@ -58,6 +60,10 @@ CASES = [
     (3, 3000, 1024, 512, 4, [3000, 2500, 700]),
     (2, 5000, 300, 256, 3, None),       # a buffer a little larger than a selection
     (2, 2000, 64, 100, 5, [2000, 90]),  # fewer slots than selected: misses stay out
+    # the measured sizes: 4096 slots and 2048 selected tokens, so the update
+    # runs its multi-pass paths (miss compaction, eligible count, victim scan
+    # over more slots and selections than one pass of its 1024 threads)
+    (2, 16384, 4096, 2048, 3, [16384, 12000]),
 ]
 
 
@@ -211,6 +217,8 @@ PF_CASES = [
     # (B, n, slots, k, candidates, steps, valid lengths)
     (3, 3000, 1024, 512, 300, 3, [3000, 2500, 700]),
     (2, 2000, 160, 100, 120, 3, [2000, 90]),  # more candidates than free slots
+    # the measured sizes: 4096 slots, k = 2048 and 2048 candidates
+    (2, 16384, 4096, 2048, 2048, 2, [16384, 9000]),
 ]
 
 
