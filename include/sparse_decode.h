@@ -105,7 +105,9 @@ typedef struct sparse_index_args {
   int64_t w_stride_b;
 
   const void* keys;   /* DOT: [B][n][D] F32/BF16; LIGHTNING: [B][n][D]
-                         E4M3FN; rows at k_stride_b / k_stride_t          */
+                         E4M3FN; rows at k_stride_b / k_stride_t.
+                         LIGHTNING: n * k_stride_t must stay below 2^31
+                         bytes (EUNSUPPORTED otherwise)                   */
   int32_t k_dtype;
   int64_t k_stride_b;
   int64_t k_stride_t;
@@ -119,7 +121,9 @@ typedef struct sparse_index_args {
   int32_t n_kv_heads;       /* Hkv                                        */
   const uint32_t* planes;   /* [B][Hkv][D][4][ceil(n/32)]: plane j of a
                                channel holds bit (3-j) of the 4-bit code;
-                               bit i of word w is token 32w + i            */
+                               bit i of word w is token 32w + i; one
+                               (request, KV head) holds below 2^31 bytes,
+                               n <= 33.5M at D = 128 (EUNSUPPORTED)        */
   const float* chan_zero;   /* [B][Hkv][D] quantizer zero (channel min)   */
   const float* chan_scale;  /* [B][Hkv][D] 4-bit cell width ((max-min)/16) */
   const float* chan_var;    /* [B][Hkv][D] channel variance var_c (unused

@@ -201,6 +201,10 @@ int check_index(const sparse_index_args* a) {
     CHECK(a->n_heads == 32 || a->n_heads == 64, SPARSE_EUNSUPPORTED,
           "LIGHTNING n_heads %d (32 or 64)", a->n_heads);
     CHECK(a->head_w && a->k_scale, SPARSE_EINVAL, "head_w / k_scale NULL");
+    // the scan addresses a request's keys with 32-bit byte offsets
+    CHECK((int64_t)a->n * a->k_stride_t <= INT32_MAX, SPARSE_EUNSUPPORTED,
+          "n * k_stride_t = %lld bytes of keys per request, above 2^31 - 1",
+          (long long)a->n * a->k_stride_t);
   }
   CHECK(a->depth_in == nullptr || a->kind == SPARSE_SCORE_BITPLANE, SPARSE_EINVAL,
         "depth_in is for kind BITPLANE only");
@@ -211,6 +215,10 @@ int check_index(const sparse_index_args* a) {
           SPARSE_EINVAL, "planes / chan_zero / chan_scale / chan_var NULL");
     CHECK(a->bit_budget >= 0 && a->bit_budget <= 4 * a->head_dim, SPARSE_EINVAL,
           "bit_budget %d outside 0..%d", a->bit_budget, 4 * a->head_dim);
+    // the scan addresses one (request, KV head)'s planes with 32-bit byte offsets
+    const int64_t plane_bytes = 16 * (int64_t)a->head_dim * ((a->n + 31) / 32);
+    CHECK(plane_bytes <= INT32_MAX, SPARSE_EUNSUPPORTED,
+          "%lld plane bytes per (request, KV head), above 2^31 - 1", (long long)plane_bytes);
   }
   return SPARSE_OK;
 }

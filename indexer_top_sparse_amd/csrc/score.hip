@@ -331,20 +331,28 @@ __global__ __launch_bounds__(kLtThreads) void score_lightning_kernel(
 
   // The K-index is streamed exactly once per step: non-temporal loads keep
   // it from displacing reusable lines in L2 and the last-level cache.
-  // Load j, lane l: row 8j + l/8 of the tile, 16-byte chunk l % 8.
+  // Load j, lane l: row 8j + l/8 of the tile, 16-byte chunk l % 8.  The
+  // request's keys and scales are read as buffers: a tile's loads take its
+  // first token's byte offset as the scalar offset and a per-lane constant
+  // as the vector offset, so no load needs address arithmetic, and rows
+  // past n read as zero (their scores are not stored).
+  const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)kb, (short)0, (int)((int64_t)n * a.k_stride_t), 0x00020000);
+  const __amdgpu_buffer_rsrc_t srsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)ksb, (short)0, n * 4, 0x00020000);
+  uint32_t kvo[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    kvo[j] = (uint32_t)(8 * j + (lane >> 3)) * (uint32_t)a.k_stride_t + 16u * (lane & 7);
   u32x4* slot = tile_s[wid];
   auto issue = [&](LtTile& tl, int it) {
-    const int tb = t0 + it * kStride;
+    const uint32_t tb = (uint32_t)(t0 + it * kStride);
+    const uint32_t koff = tb * (uint32_t)a.k_stride_t;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      int t = tb + 8 * j + (lane >> 3);
-      t = t < n ? t : n - 1;
-      tl.k[j] = __builtin_nontemporal_load(
-          (gptr<const u32x4>)(kb + (int64_t)t * a.k_stride_t + 16 * (lane & 7)));
-    }
-    int t = tb + col;
-    t = t < n ? t : n - 1;
-    tl.sc = __builtin_nontemporal_load((gptr<const float>)(ksb + t));
+    for (int j = 0; j < 4; ++j)
+      tl.k[j] = __builtin_amdgcn_raw_buffer_load_b128(krsrc, kvo[j], koff, 2 /* nt */);
+    tl.sc = __uint_as_float(
+        __builtin_amdgcn_raw_buffer_load_b32(srsrc, 4u * col, 4u * tb, 2 /* nt */));
   };
   // Re-layout through LDS: chunk c of row r sits at r*8 + (c ^ (r & 7)).
   auto transpose = [&](const LtTile& tl, u32x4 (&kk)[4]) {
@@ -625,21 +633,28 @@ hipError_t launch_read_depth(const sparse_index_args* a, int8_t* depth, int32_t*
 // ========================================================================
 // Fathom plane-prefix scan.  A thread owns one 32-bit word column of a
 // (request, KV head): 32 consecutive tokens.  The read planes (c, j) from
-// the list read_depth_kernel wrote are taken eight at a time: the workgroup
-// first tabulates, for every group of eight planes, the 256 sums of their
-// weights W_{c,j} over each subset of the group.  Per group a thread loads
-// the eight plane words (coalesced across the workgroup) and transposes the
-// 8 x 8 bit blocks inside them (three rounds of masked swaps across word
-// pairs), after which byte q of word k is the 8-bit plane index of token
-// 8q + k.  Each token then adds one table entry: two ALU ops to form the
-// LDS address, one LDS read and one add per token and group, instead of an
-// add per token and plane.  The next two groups are in flight while two are
-// processed.
+// the list read_depth_kernel wrote are taken six at a time.  For each group
+// of six the workgroup tabulates the 64 sums of their weights W_{c,j} over
+// every subset; a thread loads the six plane words (buffer loads, coalesced
+// across the workgroup), transposes the 8 x 8 bit blocks of two zero words
+// and those six words in registers, after which byte q of word k is four
+// times the 6-bit subset index of token 8q + k, and adds one table entry
+// per token.  A 64-entry
+// table puts every entry in its own LDS bank, so the lookups of a wave
+// never conflict: lanes either read different banks or share one entry.
+// (Tables of eight-plane groups, 256 entries, cost four to five LDS cycles
+// per lookup instruction from bank conflicts, which bounded the scan.)
+// The groups are taken sixteen at a time, 96 planes: their sixteen tables
+// sit at fixed LDS offsets and are rebuilt between blocks of sixteen
+// groups, so every lookup address is the token's index plus a constant.
 // ========================================================================
 constexpr int kBpThreads = 1024;
 constexpr int kBpPassTok = kBpThreads * 32;             // 32768 tokens per workgroup pass
 constexpr int kBpMaxPasses = kHistPartMax / kBpPassTok;  // per workgroup (histogram part)
-static_assert(kPlaneBatch % 8 == 0, "padded plane list: whole eight-plane groups");
+constexpr int kBpGroup = 6;                             // planes per table lookup
+constexpr int kBpBlockGroups = 16;                      // groups with resident tables
+constexpr int kBpBlockPlanes = kBpGroup * kBpBlockGroups;  // 96
+static_assert(kBpBlockGroups * 64 == kBpThreads, "one table entry per thread");
 
 int bitplane_parts(const sparse_index_args& a) {
   const int passes = (a.n + kBpPassTok - 1) / kBpPassTok;
@@ -676,15 +691,23 @@ __device__ __forceinline__ void transpose_bytes8(uint32_t (&w)[8]) {
   }
 }
 
+// One LDS buffer carved by hand, so that the tables start at address 0 and
+// a group's table base fits the LDS instructions' immediate offset.
+constexpr int kBpLdsLut = 0;                                     // [16][64] fp32
+constexpr int kBpLdsHist = kBpLdsLut + kBpBlockGroups * 64 * 4;  // [4096] u32
+constexpr int kBpLdsPoff = kBpLdsHist + kHistBins * 4;           // [512] u32
+constexpr int kBpLdsPw = kBpLdsPoff + 512 * 4;                   // [512] fp32
+constexpr int kBpLdsStage = kBpLdsPw + 512 * 4;                  // [16][1024] fp32
+constexpr int kBpLdsBytes = kBpLdsStage + (kBpThreads / 64) * 1024 * 4;
+
 __global__ __launch_bounds__(kBpThreads) void score_bitplane_kernel(
     sparse_index_args a, const int32_t* plist, const float* pwl, const int32_t* npl,
     const float* score_c, float* __restrict__ scores, uint32_t* hist, int n_units) {
-  __shared__ uint32_t hist_s[kHistBins];
-  __shared__ int32_t pl_s[512];
-  __shared__ float pw_s[512];
-  __shared__ float lut_s[512 / 8 * 256];  // [group][subset of its eight planes]
-  __shared__ __attribute__((aligned(16))) float stage_s[kBpThreads / 64][1024];  // per wave
-  LdsHist lh{hist_s};
+  __shared__ __attribute__((aligned(16))) char lds[kBpLdsBytes];
+  float* lut_s = (float*)(lds + kBpLdsLut);
+  uint32_t* poff_s = (uint32_t*)(lds + kBpLdsPoff);  // byte offset of each read plane
+  float* pw_s = (float*)(lds + kBpLdsPw);
+  LdsHist lh{(uint32_t*)(lds + kBpLdsHist)};
   const int h = blockIdx.y;
   const int b = blockIdx.z;
   const int D = a.head_dim;
@@ -694,73 +717,93 @@ __global__ __launch_bounds__(kBpThreads) void score_bitplane_kernel(
   const int valid = valid_len(a.seq_lens, b, n);
   const int64_t bh = (int64_t)b * Hkv + h;
   const int np = npl[bh];
-  // the padded list (weightless entries up to a multiple of kPlaneBatch)
-  const int npad = (np + kPlaneBatch - 1) / kPlaneBatch * kPlaneBatch;
-  for (int i = threadIdx.x; i < npad; i += kBpThreads) {
-    pl_s[i] = plist[bh * 4 * D + i];
+  // planes of one (request, KV head) span 4 D nw words (at most 64 MiB), so
+  // a plane's byte offset fits 32 bits
+  for (int i = threadIdx.x; i < np; i += kBpThreads) {
+    poff_s[i] = (uint32_t)plist[bh * 4 * D + i] * (uint32_t)nw * 4u;
     pw_s[i] = pwl[bh * 4 * D + i];
   }
   if (hist) lh.clear(kBpThreads);  // (ends with a barrier)
   else __syncthreads();
-  // subset sums of each group, in plane order
-  for (int e = threadIdx.x; e < npad / 8 * 256; e += kBpThreads) {
-    const int g = e >> 8, m = e & 255;
-    float x = 0.f;
-#pragma unroll
-    for (int k = 0; k < 8; ++k)
-      if ((m >> k) & 1) x += pw_s[8 * g + k];
-    lut_s[e] = x;
-  }
-  __syncthreads();
   const float c0 = score_c[bh];
-  const uint32_t* planes = a.planes + bh * 4 * D * (int64_t)nw;
+  // the (request, KV head)'s planes as a buffer: a load takes the plane's
+  // byte offset as its scalar offset and the lane's word column as its
+  // vector offset, so forming an address costs no vector instruction
+  const __amdgpu_buffer_rsrc_t prsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.planes + bh * 4 * D * (int64_t)nw), (short)0, (int)(4u * D * (uint32_t)nw * 4u),
+      0x00020000);
   float* srow = scores + bh * n_units;
   const int passes = (n + kBpPassTok - 1) / kBpPassTok;
+  const int nblocks = (np + kBpBlockPlanes - 1) / kBpBlockPlanes;
   for (int ps = blockIdx.x; ps < passes; ps += gridDim.x) {
     const int w = ps * kBpThreads + threadIdx.x;
     const int wc = w < nw ? w : nw - 1;  // ragged end: a valid word, result unused
+    const uint32_t wcb = 4u * (uint32_t)wc;  // the lane's byte offset in a plane
     float acc[32];
 #pragma unroll
     for (int i = 0; i < 32; ++i) acc[i] = c0;
-    auto load_group = [&](uint32_t (&wd)[8], int p0) __attribute__((always_inline)) {
+    for (int blk = 0; blk < nblocks; ++blk) {
+      const int pb = blk * kBpBlockPlanes;  // first plane of the block
+      // the six words of group g of the block: every lane reads the same
+      // plane (a wave-uniform base) at its own word column; planes past np
+      // (the last group's tail) repeat the last read plane, whose table
+      // bits weigh 0
+      auto load_group = [&](uint32_t (&wd)[kBpGroup], int g) __attribute__((always_inline)) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k)
-        wd[k] = __builtin_nontemporal_load(planes + (int64_t)pl_s[p0 + k] * nw + wc);
-    };
-    auto add_group = [&](uint32_t (&wd)[8], int p0) __attribute__((always_inline)) {
-      transpose_bytes8(wd);
-      const float* lut = lut_s + (p0 >> 3) * 256;
+        for (int k = 0; k < kBpGroup; ++k) {
+          const int pi = min(pb + kBpGroup * g + k, np - 1);
+          const uint32_t off = __builtin_amdgcn_readfirstlane(poff_s[pi]);
+          wd[k] = __builtin_amdgcn_raw_buffer_load_b32(prsrc, wcb, off, 2 /* nt */);
+        }
+      };
+      const int ng = min(kBpBlockGroups, (np - pb + kBpGroup - 1) / kBpGroup);
+      // the first two groups' loads go out before the tables are built
+      uint32_t ring[3][kBpGroup];
+      load_group(ring[0], 0);
+      if (ng > 1) load_group(ring[1], 1);
+      __syncthreads();  // the previous block's lookups are done
+      {
+        // table entry e = group e / 64, subset e % 64 of its six planes
+        const int g = threadIdx.x >> 6, m = threadIdx.x & 63;
+        float x = 0.f;
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
+        for (int j = 0; j < kBpGroup; ++j) {
+          const int pi = pb + kBpGroup * g + j;
+          if (((m >> j) & 1) && pi < np) x += pw_s[pi];
+        }
+        lut_s[threadIdx.x] = x;
+      }
+      __syncthreads();
 #pragma unroll
-        for (int k = 0; k < 8; ++k) acc[8 * q + k] += lut[(wd[k] >> (8 * q)) & 0xFFu];
-    };
-    // two groups per step, the next two in flight (npad is a multiple of 8,
-    // so the last step may hold only one)
-    constexpr int QG = 2;
-    uint32_t cur[QG][8];
+      for (int g = 0; g < kBpBlockGroups; ++g) {
+        if (g < ng) {
+          if (g + 2 < ng) load_group(ring[(g + 2) % 3], g + 2);
+          // two zero words, then the six planes: after the transpose bit
+          // j + 2 of byte q of w8[k] is plane j's bit of token 8q + k and
+          // bits 0 and 1 are zero, so the byte is four times the token's
+          // subset index, i.e. its byte offset in group g's table, which
+          // starts at LDS address 256 g
+          uint32_t w8[8];
+          w8[0] = 0u;
+          w8[1] = 0u;
 #pragma unroll
-    for (int gq = 0; gq < QG; ++gq)
-      if (8 * gq < npad) load_group(cur[gq], 8 * gq);
-    for (int p0 = 0; p0 < npad; p0 += 8 * QG) {
-      uint32_t nxt[QG][8];
+          for (int k = 0; k < kBpGroup; ++k) w8[2 + k] = ring[g % 3][k];
+          transpose_bytes8(w8);
 #pragma unroll
-      for (int gq = 0; gq < QG; ++gq)
-        if (p0 + 8 * QG + 8 * gq < npad) load_group(nxt[gq], p0 + 8 * QG + 8 * gq);
+          for (int k = 0; k < 8; ++k)
 #pragma unroll
-      for (int gq = 0; gq < QG; ++gq)
-        if (p0 + 8 * gq < npad) add_group(cur[gq], p0 + 8 * gq);
-#pragma unroll
-      for (int gq = 0; gq < QG; ++gq)
-#pragma unroll
-        for (int k = 0; k < 8; ++k) cur[gq][k] = nxt[gq][k];
+            for (int q = 0; q < 4; ++q)
+              acc[8 * q + k] +=
+                  *(const float*)(lds + kBpLdsLut + 256 * g + ((w8[k] >> (8 * q)) & 0xFFu));
+        }
+      }
     }
     // A lane holds 32 consecutive tokens, so stores straight from acc would
     // touch 64 cache lines per instruction.  The wave's 2048 tokens pass
     // through its LDS slot instead, 1024 at a time (the lanes of one half,
     // rows of 32 tokens, 16-byte chunks XOR-swizzled by row), and leave as
     // coalesced 256-byte stores.
-    float* st = stage_s[threadIdx.x >> 6];
+    float* st = (float*)(lds + kBpLdsStage) + (threadIdx.x >> 6) * 1024;
     const int lane = threadIdx.x & 63;
     const int t_wave = 32 * (w - lane);  // first token of the wave
 #pragma unroll
