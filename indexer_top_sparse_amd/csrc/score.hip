@@ -332,10 +332,12 @@ __global__ __launch_bounds__(kLtThreads) void score_lightning_kernel(
   // The K-index is streamed exactly once per step: non-temporal loads keep
   // it from displacing reusable lines in L2 and the last-level cache.
   // Load j, lane l: row 8j + l/8 of the tile, 16-byte chunk l % 8.  The
-  // request's keys and scales are read as buffers: a tile's loads take its
-  // first token's byte offset as the scalar offset and a per-lane constant
-  // as the vector offset, so no load needs address arithmetic, and rows
-  // past n read as zero (their scores are not stored).
+  // request's keys and scales are read as buffers.  In a wave whose tiles
+  // all lie below n, a tile's loads take its first token's byte offset as
+  // the scalar offset and a per-lane constant as the vector offset, so no
+  // load needs address arithmetic.  The ragged last wave puts the whole
+  // offset in the vector operand instead: the buffer's range check then
+  // turns every row past n into zeros (their scores are not stored).
   const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)kb, (short)0, (int)((int64_t)n * a.k_stride_t), 0x00020000);
   const __amdgpu_buffer_rsrc_t srsrc =
@@ -353,6 +355,15 @@ __global__ __launch_bounds__(kLtThreads) void score_lightning_kernel(
       tl.k[j] = __builtin_amdgcn_raw_buffer_load_b128(krsrc, kvo[j], koff, 2 /* nt */);
     tl.sc = __uint_as_float(
         __builtin_amdgcn_raw_buffer_load_b32(srsrc, 4u * col, 4u * tb, 2 /* nt */));
+  };
+  auto issue_ragged = [&](LtTile& tl, int it) {
+    const uint32_t tb = (uint32_t)(t0 + it * kStride);
+    const uint32_t koff = tb * (uint32_t)a.k_stride_t;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      tl.k[j] = __builtin_amdgcn_raw_buffer_load_b128(krsrc, kvo[j] + koff, 0, 2 /* nt */);
+    tl.sc = __uint_as_float(
+        __builtin_amdgcn_raw_buffer_load_b32(srsrc, 4u * (tb + col), 0, 2 /* nt */));
   };
   // Re-layout through LDS: chunk c of row r sits at r*8 + (c ^ (r & 7)).
   auto transpose = [&](const LtTile& tl, u32x4 (&kk)[4]) {
@@ -447,7 +458,7 @@ __global__ __launch_bounds__(kLtThreads) void score_lightning_kernel(
     for (int s = 0; s < kLtStages; ++s) consume(buf[s], TPW - kLtStages + s);
   } else {
     for (int it = 0; it < ntiles; ++it) {
-      issue(buf[0], it);
+      issue_ragged(buf[0], it);
       consume(buf[0], it);
     }
   }
