@@ -89,7 +89,8 @@ enum sparse_score_kind {
 typedef struct sparse_index_args {
   int32_t kind;            /* enum sparse_score_kind */
   int32_t batch;           /* B >= 0 */
-  int32_t n;               /* token capacity per request, n >= 0 */
+  int32_t n;               /* token capacity per request, 0 <= n <= 4194304
+                              (EUNSUPPORTED above) */
   const int32_t* seq_lens; /* [B] valid tokens per request (<= n); NULL = n */
 
   int32_t n_heads;  /* DOT/LIGHTNING: index query heads H.  BITPLANE: the
@@ -121,9 +122,7 @@ typedef struct sparse_index_args {
   int32_t n_kv_heads;       /* Hkv                                        */
   const uint32_t* planes;   /* [B][Hkv][D][4][ceil(n/32)]: plane j of a
                                channel holds bit (3-j) of the 4-bit code;
-                               bit i of word w is token 32w + i; one
-                               (request, KV head) holds below 2^31 bytes,
-                               n <= 33.5M at D = 128 (EUNSUPPORTED)        */
+                               bit i of word w is token 32w + i            */
   const float* chan_zero;   /* [B][Hkv][D] quantizer zero (channel min)   */
   const float* chan_scale;  /* [B][Hkv][D] 4-bit cell width ((max-min)/16) */
   const float* chan_var;    /* [B][Hkv][D] channel variance var_c (unused

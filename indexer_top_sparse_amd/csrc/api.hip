@@ -215,10 +215,6 @@ int check_index(const sparse_index_args* a) {
           SPARSE_EINVAL, "planes / chan_zero / chan_scale / chan_var NULL");
     CHECK(a->bit_budget >= 0 && a->bit_budget <= 4 * a->head_dim, SPARSE_EINVAL,
           "bit_budget %d outside 0..%d", a->bit_budget, 4 * a->head_dim);
-    // the scan addresses one (request, KV head)'s planes with 32-bit byte offsets
-    const int64_t plane_bytes = 16 * (int64_t)a->head_dim * ((a->n + 31) / 32);
-    CHECK(plane_bytes <= INT32_MAX, SPARSE_EUNSUPPORTED,
-          "%lld plane bytes per (request, KV head), above 2^31 - 1", (long long)plane_bytes);
   }
   return SPARSE_OK;
 }

@@ -128,6 +128,18 @@ def test_index_validation_codes():
     assert L.sparse_index_score(ctypes.byref(a), FAKE, FAKE, 1 << 30, None) == \
         isa.SPARSE_EINVAL
     assert L.sparse_abi_version() == 2
+    # at most 4194304 tokens per request
+    a = _lightning(n=(1 << 22) + 1)
+    assert L.sparse_workspace_size(ctypes.byref(a), None, 1, ctypes.byref(out)) == \
+        isa.SPARSE_EUNSUPPORTED
+    # the fp8 scan addresses one request's keys with 32-bit byte offsets:
+    # padded rows that take a request past 2^31 bytes are refused
+    a = _lightning(n=1 << 22)
+    a.k_stride_t = 512  # 2 GiB of keys per request
+    assert L.sparse_workspace_size(ctypes.byref(a), None, 1, ctypes.byref(out)) == \
+        isa.SPARSE_EUNSUPPORTED
+    a.k_stride_t = 496  # below 2^31 bytes
+    assert L.sparse_workspace_size(ctypes.byref(a), None, 1, ctypes.byref(out)) == isa.SPARSE_OK
     # empty batch: nothing to do, nothing launched
     a = _lightning(B=0)
     assert L.sparse_index_score(ctypes.byref(a), None, None, 0, None) == isa.SPARSE_OK
