@@ -226,10 +226,9 @@ int sparse_read_depth(const sparse_index_args* ia, int8_t* depth_out,
  * sparse_read_depth).  scores: [B][R][n_units] fp32, device, caller-owned,
  * with R = 1 (DOT, LIGHTNING) or R = Hkv (BITPLANE) and n_units =
  * ceil(n / block_size).  Units at or past a request's valid length are
- * written as -inf.  ws: needed (sparse_workspace_size with only `ia`) for
- * BITPLANE, which keeps the read depths and plane weights there; may be
- * NULL for the other kinds.  Errors: EINVAL / EUNSUPPORTED from the
- * argument checks, EWORKSPACE, EHIP. */
+ * written as -inf.  ws, ws_bytes: not used by any kind (the bit-plane scan
+ * selects its read depths in its own prologue); may be NULL / 0.  Errors:
+ * EINVAL / EUNSUPPORTED from the argument checks, EHIP. */
 int sparse_index_score(const sparse_index_args* ia, float* scores, void* ws,
                        size_t ws_bytes, void* stream);
 

@@ -64,7 +64,7 @@ struct IndexLayout {
   int n_chunks = 0;
   int hist_parts = 0;   // histogram parts per row the score kernel writes
   size_t scores = 0, hist = 0, bstar = 0, cand_key = 0, cand_idx = 0, chunk_cnt = 0,
-         cand_total = 0, depth = 0, plist = 0, pwl = 0, npl = 0, score_c = 0, end = 0;
+         cand_total = 0, end = 0;
 };
 
 IndexLayout index_layout(const sparse_index_args& a, bool with_scores) {
@@ -88,14 +88,6 @@ IndexLayout index_layout(const sparse_index_args& a, bool with_scores) {
   L.cand_idx = take(cells * 4);
   L.chunk_cnt = take((size_t)L.rows * std::max(L.n_chunks, 1) * 4);
   L.cand_total = take((size_t)L.rows * 4);
-  if (a.kind == SPARSE_SCORE_BITPLANE) {
-    const size_t hd = (size_t)a.batch * a.n_kv_heads * a.head_dim;
-    L.depth = take(hd);
-    L.plist = take(hd * 4 * 4);
-    L.pwl = take(hd * 4 * 4);
-    L.npl = take((size_t)a.batch * a.n_kv_heads * 4);
-    L.score_c = take((size_t)a.batch * a.n_kv_heads * 4);
-  }
   L.end = off;
   return L;
 }
@@ -321,8 +313,8 @@ int run_topk(const sd::TopkPlan& p, bool hist_ready, hipStream_t s) {
   return SPARSE_OK;
 }
 
-int run_scores(const sparse_index_args& a, const IndexLayout& L, char* ws, float* scores,
-               uint32_t* hist, hipStream_t s) {
+int run_scores(const sparse_index_args& a, const IndexLayout& L, float* scores, uint32_t* hist,
+               hipStream_t s) {
   sd::ScorePlan sp;
   sp.a = &a;
   sp.scores = scores;
@@ -341,12 +333,7 @@ int run_scores(const sparse_index_args& a, const IndexLayout& L, char* ws, float
       HIPCHECK(sd::launch_score_lightning(sp, s));
       break;
     case SPARSE_SCORE_BITPLANE:
-      sp.depth = (int8_t*)(ws + L.depth);
-      sp.plist = (int32_t*)(ws + L.plist);
-      sp.pwl = (float*)(ws + L.pwl);
-      sp.npl = (int32_t*)(ws + L.npl);
-      sp.score_c = (float*)(ws + L.score_c);
-      HIPCHECK(sd::launch_read_depth(&a, sp.depth, sp.plist, sp.pwl, sp.npl, sp.score_c, s));
+      // the scan selects the read depth in its own prologue (no plane list)
       HIPCHECK(sd::launch_score_bitplane(sp, s));
       break;
   }
@@ -469,11 +456,10 @@ int sparse_index_score(const sparse_index_args* ia, float* scores, void* ws,
   if (rc) return rc;
   if (ia->batch == 0 || ia->n == 0) return SPARSE_OK;
   CHECK(scores, SPARSE_EINVAL, "scores NULL");
+  (void)ws;
+  (void)ws_bytes;
   IndexLayout L = index_layout(*ia, false);
-  if (ia->kind == SPARSE_SCORE_BITPLANE) {
-    CHECK(ws && ws_bytes >= L.end, SPARSE_EWORKSPACE, "workspace %zu < %zu", ws_bytes, L.end);
-  }
-  return run_scores(*ia, L, (char*)ws, scores, nullptr, (hipStream_t)stream);
+  return run_scores(*ia, L, scores, nullptr, (hipStream_t)stream);
 }
 
 int sparse_topk(const float* scores, int32_t rows, int32_t n_units, int64_t row_stride,
@@ -536,7 +522,7 @@ int sparse_decode_step(const sparse_index_args* ia, const sparse_attn_args* aa, 
                                    unit, k, topk_out, nullptr, L.hist_parts,
                                    sd::score_part_span(*ia));
   if (ia->n > 0) {
-    rc = run_scores(*ia, L, w, scores, tp.direct ? nullptr : tp.hist, s);
+    rc = run_scores(*ia, L, scores, tp.direct ? nullptr : tp.hist, s);
     if (rc) return rc;
   }
   rc = run_topk(tp, true, s);

@@ -512,30 +512,43 @@ hipError_t launch_score_lightning(const ScorePlan& p, hipStream_t s) {
 constexpr int kDepthThreads = 512;  // D = 128 channels x 4 planes
 constexpr int kPlaneBatch = 8;      // plane-list entries the scan fetches at once
 
-__global__ __launch_bounds__(kDepthThreads) void read_depth_kernel(
-    sparse_index_args a, int8_t* __restrict__ depth, int32_t* __restrict__ plist,
-    float* __restrict__ pwl, int32_t* __restrict__ npl, float* __restrict__ score_c) {
-  __shared__ double gain_s[kDepthThreads];
-  __shared__ double qbar_s[128];
-  __shared__ int taken_s[kDepthThreads];
-  __shared__ double cterm_s[128];
-  __shared__ int scan_s[kDepthThreads / 64 + 1];
-  const int h = blockIdx.x;
-  const int b = blockIdx.y;
+// LDS of the read-depth selection of one (request, KV head).
+struct DepthLds {
+  double gain[kDepthThreads];
+  double qbar[128];
+  double cterm[128];
+  int taken[kDepthThreads];
+  int scan[kDepthThreads / 64 + 1];
+};
+
+// The read depth of (request b, KV head h), left in LDS: L.taken[4c + j] is
+// 1 when plane j of channel c is read, L.qbar[c] is q_bar_c and L.cterm[c]
+// the channel's score constant q_bar_c * (zero_c + cell_c * 2^(3 - t_c)).
+// Thread tid < 512 stands for (channel tid / 4, plane tid % 4) and gets that
+// channel's cell width in cell; depth (nullable) receives t_c.  Every thread
+// of the NT-thread workgroup must call it (it holds block barriers); it
+// ends with a barrier.
+template <int NT>
+__device__ void depth_select(const sparse_index_args& a, int b, int h, DepthLds& L,
+                             float& cell, int8_t* depth) {
+  static_assert(NT >= kDepthThreads, "one thread per (channel, plane)");
   const int D = a.head_dim;
   const int Hkv = a.n_kv_heads;
   const int G = a.n_heads / Hkv;
   const int tid = threadIdx.x;
-  const int c = tid >> 2;
+  // waves past the 512 (channel, plane) threads only join the barriers; the
+  // test is on the wave's first lane, so those waves branch around the work
+  const bool act = __builtin_amdgcn_readfirstlane(tid) < kDepthThreads;
+  const int c = (tid & (kDepthThreads - 1)) >> 2;
   const int j = tid & 3;
   const int64_t hd = ((int64_t)b * Hkv + h) * D;
   // every global input first (one round trip): this thread's channel c
   // (variance, or the given depth) and, for tid < D, channel tid's cell and
   // zero point
   const bool fixed = a.depth_in != nullptr;
-  const float var_c = (!fixed && c < D) ? a.chan_var[hd + c] : 0.f;
-  const int din_c = (fixed && c < D) ? (int)a.depth_in[hd + c] : 0;
-  const float cell_c = c < D ? a.chan_scale[hd + c] : 0.f;
+  const float var_c = (act && !fixed && c < D) ? a.chan_var[hd + c] : 0.f;
+  const int din_c = (act && fixed && c < D) ? (int)a.depth_in[hd + c] : 0;
+  cell = (act && c < D) ? a.chan_scale[hd + c] : 0.f;
   const float cell_t = tid < D ? a.chan_scale[hd + tid] : 0.f;
   const float zero_t = tid < D ? a.chan_zero[hd + tid] : 0.f;
   if (tid < D) {
@@ -544,74 +557,138 @@ __global__ __launch_bounds__(kDepthThreads) void read_depth_kernel(
     double acc = (double)bf16_bits_to_f32(q0[tid]);
     for (int gq = 1; gq < G; ++gq)
       acc = __dadd_rn(acc, (double)bf16_bits_to_f32(q0[(int64_t)gq * a.q_stride_h + tid]));
-    qbar_s[tid] = acc;
+    L.qbar[tid] = acc;
   }
   __syncthreads();
-  if (!fixed && c < D) {
-    double qb = qbar_s[c];
+  if (act && !fixed && c < D) {
+    double qb = L.qbar[c];
     double imp = __dmul_rn(__dmul_rn(qb, qb), (double)var_c);
-    gain_s[tid] = ldexp(imp, -2 * j);
+    L.gain[tid] = ldexp(imp, -2 * j);
   }
   __syncthreads();
   if (fixed) {
     // a fixed allocation from the caller: planes j < t_c of channel c
     const int tc = c < D ? min(max(din_c, 0), 4) : 0;
-    taken_s[tid] = j < tc;
+    if (act) L.taken[tid] = j < tc;
     __syncthreads();
   } else {
-  // Rank every gain in the total order (gain desc, channel asc, plane asc)
-  // -- index order tid = 4c + j is (channel, plane) ascending -- with a
-  // bitonic sort of (gain, index) pairs: position r of the sorted list holds
-  // the gain of rank r.  Slots past 4D hold -1 (below every gain).  Steps
-  // between lanes of one wave exchange through DPP and lane swaps; only the
-  // six steps that cross waves go through LDS and barriers.
-  {
-    double key = c < D ? gain_s[tid] : -1.0;
+    // Rank every gain in the total order (gain desc, channel asc, plane asc)
+    // -- index order tid = 4c + j is (channel, plane) ascending -- with a
+    // bitonic sort of (gain, index) pairs: position r of the sorted list
+    // holds the gain of rank r.  Slots past 4D hold -1 (below every gain).
+    // Steps between lanes of one wave exchange through DPP and lane swaps;
+    // only the six steps that cross waves go through LDS and barriers.
+    // (Sorting each wave's 64 pairs and ranking by binary searches in the
+    // other waves' sorted lists measured slower.)
+    double key = (act && c < D) ? L.gain[tid] : -1.0;
     int id = tid;
 #pragma unroll
     for (int k = 2; k <= kDepthThreads; k <<= 1) {
 #pragma unroll
       for (int jj = k >> 1; jj > 0; jj >>= 1) {
         const int o = tid ^ jj;
-        double ko;
-        int io;
+        double ko = key;
+        int io = id;
         if (jj >= kWave) {  // partner in another wave: through LDS
           __syncthreads();
-          gain_s[tid] = key;
-          taken_s[tid] = id;
+          if (act) {
+            L.gain[tid] = key;
+            L.taken[tid] = id;
+          }
           __syncthreads();
-          ko = gain_s[o];
-          io = taken_s[o];
-        } else {  // partner in this wave: DPP / lane swaps, no barrier
+          if (act) {
+            ko = L.gain[o];
+            io = L.taken[o];
+          }
+        } else if (act) {  // partner in this wave: DPP / lane swaps, no barrier
           const uint2 kb = __builtin_bit_cast(uint2, key);
           ko = __builtin_bit_cast(double, make_uint2(lane_xor_u32(kb.x, jj), lane_xor_u32(kb.y, jj)));
           io = (int)lane_xor_u32((uint32_t)id, jj);
         }
-        const bool mine_first = (key > ko) || (key == ko && id < io);
-        // the lower slot of an ascending block keeps the earlier element
-        const bool keep_first = ((tid & k) == 0) == (tid < o);
-        if (mine_first != keep_first) { key = ko; id = io; }
+        if (act) {
+          const bool mine_first = (key > ko) || (key == ko && id < io);
+          // the lower slot of an ascending block keeps the earlier element
+          const bool keep_first = ((tid & k) == 0) == (tid < o);
+          if (mine_first != keep_first) { key = ko; id = io; }
+        }
       }
     }
     __syncthreads();
-    taken_s[id] = tid < a.bit_budget;  // element id has rank tid
+    if (act) L.taken[id] = tid < a.bit_budget;  // element id has rank tid
     __syncthreads();
   }
-  }
-  const int taken = c < D ? taken_s[tid] : 0;
   if (tid < D) {
-    int t = taken_s[4 * tid] + taken_s[4 * tid + 1] + taken_s[4 * tid + 2] +
-            taken_s[4 * tid + 3];
-    depth[hd + tid] = (int8_t)t;
-    double qb = qbar_s[tid];
-    cterm_s[tid] = qb * ((double)zero_t + (double)cell_t * ldexp(1.0, 3 - t));
+    const int t = L.taken[4 * tid] + L.taken[4 * tid + 1] + L.taken[4 * tid + 2] +
+                  L.taken[4 * tid + 3];
+    if (depth) depth[hd + tid] = (int8_t)t;
+    L.cterm[tid] = L.qbar[tid] * ((double)zero_t + (double)cell_t * ldexp(1.0, 3 - t));
   }
+  __syncthreads();
+}
+
+// sum_c cterm_c as a fixed pairwise tree over the 128 channels (level w
+// adds entry t + w into entry t), left in L.cterm[0].  Every thread calls
+// it; it ends with a barrier.  With D = 128 the first wave holds the
+// level-64 sums, one per lane, and the lower levels pair lanes l and l + w
+// with lane swaps: the same additions in the same order, without barriers.
+__device__ __forceinline__ double lane_xor_f64(double v, int m) {
+  const uint2 u = __builtin_bit_cast(uint2, v);
+  return __builtin_bit_cast(double, make_uint2(lane_xor_u32(u.x, m), lane_xor_u32(u.y, m)));
+}
+__device__ __forceinline__ void depth_constant(DepthLds& L, int D) {
+  if (D == 2 * kWave) {
+    if (threadIdx.x < kWave) {
+      double x = L.cterm[threadIdx.x] + L.cterm[threadIdx.x + kWave];
+#pragma unroll
+      for (int w = kWave / 2; w >= 1; w >>= 1) {
+        const double other = lane_xor_f64(x, w);  // lane l + w for l < w
+        x = x + other;
+      }
+      if (threadIdx.x == 0) L.cterm[0] = x;
+    }
+    __syncthreads();
+    return;
+  }
+  for (int w = D / 2; w >= 1; w >>= 1) {
+    if ((int)threadIdx.x < w) L.cterm[threadIdx.x] += L.cterm[threadIdx.x + w];
+    __syncthreads();
+  }
+}
+
+// ========================================================================
+// Fathom read depth: one workgroup per (request, KV head), one thread per
+// (channel, plane) gain.  All arithmetic that decides the allocation is
+// float64 with a fixed operation order: q_bar = ((q_0 + q_1) + ...),
+// imp = (q_bar * q_bar) * var, gain = imp * 4^-j (an exact power-of-two
+// scaling); those are exact for bf16 queries and fp32 variances, so the
+// ranking (gain desc, channel asc, plane asc) is reproducible bit for bit.
+// The workgroup also turns the depths into the scan's plane weights
+// W_{c,j} = q_bar_c * cell_c * 2^(3-j) for read planes and the constant
+// sum_c q_bar_c * (zero_c + cell_c * 2^(3 - t_c)).  The fused step's scan
+// does the same work in its own prologue (score_bitplane_kernel); this
+// kernel serves sparse_read_depth.
+// ========================================================================
+__global__ __launch_bounds__(kDepthThreads) void read_depth_kernel(
+    sparse_index_args a, int8_t* __restrict__ depth, int32_t* __restrict__ plist,
+    float* __restrict__ pwl, int32_t* __restrict__ npl, float* __restrict__ score_c) {
+  __shared__ DepthLds L;
+  const int h = blockIdx.x;
+  const int b = blockIdx.y;
+  const int D = a.head_dim;
+  const int Hkv = a.n_kv_heads;
+  const int tid = threadIdx.x;
+  const int c = tid >> 2;
+  const int j = tid & 3;
+  const int64_t hd = ((int64_t)b * Hkv + h) * D;
+  float cell_c;
+  depth_select<kDepthThreads>(a, b, h, L, cell_c, depth);
+  const int taken = c < D ? L.taken[tid] : 0;
   if (plist) {
     // read planes in (channel, plane) order with the weight of their bit
     int total;
-    const int incl = block_inclusive_scan<kDepthThreads>(taken, scan_s, &total);
+    const int incl = block_inclusive_scan<kDepthThreads>(taken, L.scan, &total);
     if (taken) {
-      const double qb = qbar_s[c];
+      const double qb = L.qbar[c];
       plist[hd * 4 + incl - 1] = tid;
       pwl[hd * 4 + incl - 1] = (float)(qb * (double)cell_c * ldexp(1.0, 3 - j));
     }
@@ -623,14 +700,9 @@ __global__ __launch_bounds__(kDepthThreads) void read_depth_kernel(
       pwl[hd * 4 + tid] = 0.f;
     }
   }
-  __syncthreads();
-  // sum_c cterm_c as a fixed pairwise tree over the 128 channels
   if (score_c) {
-    for (int w = D / 2; w >= 1; w >>= 1) {
-      if (tid < w) cterm_s[tid] += cterm_s[tid + w];
-      __syncthreads();
-    }
-    if (tid == 0) score_c[(int64_t)b * Hkv + h] = (float)cterm_s[0];
+    depth_constant(L, D);
+    if (tid == 0) score_c[(int64_t)b * Hkv + h] = (float)L.cterm[0];
   }
 }
 
@@ -643,8 +715,12 @@ hipError_t launch_read_depth(const sparse_index_args* a, int8_t* depth, int32_t*
 
 // ========================================================================
 // Fathom plane-prefix scan.  A thread owns one 32-bit word column of a
-// (request, KV head): 32 consecutive tokens.  The read planes (c, j) from
-// the list read_depth_kernel wrote are taken six at a time.  For each group
+// (request, KV head): 32 consecutive tokens.  The workgroup first selects
+// the read depths itself (depth_select, the same selection as
+// read_depth_kernel, repeated by every workgroup of the (request, KV head):
+// cheaper than a launch of its own); a plane list written by
+// read_depth_kernel can be passed instead.  The read planes (c, j) are
+// taken six at a time.  For each group
 // of six the workgroup tabulates the 64 sums of their weights W_{c,j} over
 // every subset; a thread loads the six plane words (buffer loads, coalesced
 // across the workgroup), transposes the 8 x 8 bit blocks of two zero words
@@ -710,6 +786,8 @@ constexpr int kBpLdsPoff = kBpLdsHist + kHistBins * 4;           // [512] u32
 constexpr int kBpLdsPw = kBpLdsPoff + 512 * 4;                   // [512] fp32
 constexpr int kBpLdsStage = kBpLdsPw + 512 * 4;                  // [16][1024] fp32
 constexpr int kBpLdsBytes = kBpLdsStage + (kBpThreads / 64) * 1024 * 4;
+static_assert(sizeof(DepthLds) <= kBpLdsBytes - kBpLdsStage && kBpLdsStage % 8 == 0,
+              "the read-depth selection fits the staging LDS");
 
 __global__ __launch_bounds__(kBpThreads) void score_bitplane_kernel(
     sparse_index_args a, const int32_t* plist, const float* pwl, const int32_t* npl,
@@ -727,16 +805,41 @@ __global__ __launch_bounds__(kBpThreads) void score_bitplane_kernel(
   const int nw = (n + 31) / 32;
   const int valid = valid_len(a.seq_lens, b, n);
   const int64_t bh = (int64_t)b * Hkv + h;
-  const int np = npl[bh];
-  // planes of one (request, KV head) span 4 D nw words (at most 64 MiB), so
+  // planes of one (request, KV head) span 4 D nw words (at most 16 MiB), so
   // a plane's byte offset fits 32 bits
-  for (int i = threadIdx.x; i < np; i += kBpThreads) {
-    poff_s[i] = (uint32_t)plist[bh * 4 * D + i] * (uint32_t)nw * 4u;
-    pw_s[i] = pwl[bh * 4 * D + i];
+  int np;
+  float c0;
+  if (plist) {
+    // the plane list read_depth_kernel wrote
+    np = npl[bh];
+    for (int i = threadIdx.x; i < np; i += kBpThreads) {
+      poff_s[i] = (uint32_t)plist[bh * 4 * D + i] * (uint32_t)nw * 4u;
+      pw_s[i] = pwl[bh * 4 * D + i];
+    }
+    if (hist) lh.clear(kBpThreads);  // (ends with a barrier)
+    else __syncthreads();
+    c0 = score_c[bh];
+  } else {
+    // the read depth computed here, in the LDS the score staging uses later:
+    // every workgroup of the (request, KV head) repeats the same selection,
+    // which costs less than a launch of its own
+    DepthLds& L = *(DepthLds*)(lds + kBpLdsStage);
+    float cell;
+    depth_select<kBpThreads>(a, b, h, L, cell, nullptr);
+    const int tid = threadIdx.x;
+    const int taken = tid < kDepthThreads && (tid >> 2) < D ? L.taken[tid] : 0;
+    int total;
+    const int incl = block_inclusive_scan<kBpThreads>(taken, L.scan, &total);
+    if (taken) {
+      poff_s[incl - 1] = (uint32_t)tid * (uint32_t)nw * 4u;
+      pw_s[incl - 1] = (float)(L.qbar[tid >> 2] * (double)cell * ldexp(1.0, 3 - (tid & 3)));
+    }
+    np = total;
+    depth_constant(L, D);
+    c0 = (float)L.cterm[0];
+    if (hist) lh.clear(kBpThreads);  // (ends with a barrier)
+    else __syncthreads();
   }
-  if (hist) lh.clear(kBpThreads);  // (ends with a barrier)
-  else __syncthreads();
-  const float c0 = score_c[bh];
   // the (request, KV head)'s planes as a buffer: a load takes the plane's
   // byte offset as its scalar offset and the lane's word column as its
   // vector offset, so forming an address costs no vector instruction
