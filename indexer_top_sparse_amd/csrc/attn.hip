@@ -594,7 +594,9 @@ struct GqaTile {
   u32x4 v[8];     // V row (lane / 16) + 4 u, 16-byte chunk lane % 16
 };
 
-__global__ __launch_bounds__(64 * kGqaWaves) void attn_gqa_kernel(AttnPlan p) {
+// (At most 256 VGPRs, so that two workgroups share a compute unit: at 260
+// the kernel ran one workgroup per unit.)
+__global__ __launch_bounds__(64 * kGqaWaves, 2) void attn_gqa_kernel(AttnPlan p) {
   __shared__ __attribute__((aligned(16))) uint16_t vs_s[kGqaWaves][kTT * kGqaRowV];
   __shared__ uint64_t rowp_s[kMaxSplitTok];
   __shared__ uint32_t vmask_s[kMaxSplitTok / kTT];
