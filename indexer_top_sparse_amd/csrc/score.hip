@@ -140,7 +140,9 @@ int dot_parts(const sparse_index_args& a) {
 }
 
 template <typename T, int BLOCK>
-__global__ __launch_bounds__(kDotThreads) void score_dot_kernel(
+// (At most 168 VGPRs: three waves per SIMD.  The bf16 block-max variant
+// compiled to 169, i.e. two.)
+__global__ __launch_bounds__(kDotThreads, 3) void score_dot_kernel(
     sparse_index_args a, float* __restrict__ scores, uint32_t* hist, int n_units,
     int rounds) {
   constexpr int LPR = DotTraits<T>::kLPR;
