@@ -517,6 +517,8 @@ constexpr int kPlaneBatch = 8;      // plane-list entries the scan fetches at on
 // LDS of the read-depth selection of one (request, KV head).
 struct DepthLds {
   double gain[kDepthThreads];
+  double xkey[kDepthThreads];  // second exchange buffer of the sort
+  int xid[2][kDepthThreads];   // indices of the two exchange buffers
   double qbar[128];
   double cterm[128];
   int taken[kDepthThreads];
@@ -579,11 +581,15 @@ __device__ void depth_select(const sparse_index_args& a, int b, int h, DepthLds&
     // bitonic sort of (gain, index) pairs: position r of the sorted list
     // holds the gain of rank r.  Slots past 4D hold -1 (below every gain).
     // Steps between lanes of one wave exchange through DPP and lane swaps;
-    // only the six steps that cross waves go through LDS and barriers.
+    // only the six steps that cross waves go through LDS and a barrier.
     // (Sorting each wave's 64 pairs and ranking by binary searches in the
     // other waves' sorted lists measured slower.)
+    // The steps across waves alternate between two exchange buffers, so
+    // each needs one barrier: a buffer is written again two such steps
+    // later, after every wave has passed the barrier of the step between.
     double key = (act && c < D) ? L.gain[tid] : -1.0;
     int id = tid;
+    int xs = 0;  // steps across waves so far (resolved at compile time)
 #pragma unroll
     for (int k = 2; k <= kDepthThreads; k <<= 1) {
 #pragma unroll
@@ -592,16 +598,18 @@ __device__ void depth_select(const sparse_index_args& a, int b, int h, DepthLds&
         double ko = key;
         int io = id;
         if (jj >= kWave) {  // partner in another wave: through LDS
-          __syncthreads();
+          double* xk = (xs & 1) ? L.xkey : L.gain;
+          int* xi = L.xid[xs & 1];
           if (act) {
-            L.gain[tid] = key;
-            L.taken[tid] = id;
+            xk[tid] = key;
+            xi[tid] = id;
           }
           __syncthreads();
           if (act) {
-            ko = L.gain[o];
-            io = L.taken[o];
+            ko = xk[o];
+            io = xi[o];
           }
+          ++xs;
         } else if (act) {  // partner in this wave: DPP / lane swaps, no barrier
           const uint2 kb = __builtin_bit_cast(uint2, key);
           ko = __builtin_bit_cast(double, make_uint2(lane_xor_u32(kb.x, jj), lane_xor_u32(kb.y, jj)));
@@ -615,7 +623,6 @@ __device__ void depth_select(const sparse_index_args& a, int b, int h, DepthLds&
         }
       }
     }
-    __syncthreads();
     if (act) L.taken[id] = tid < a.bit_budget;  // element id has rank tid
     __syncthreads();
   }
