@@ -100,6 +100,26 @@ def test_lightning_128k_full():
     _rerun_identical(r)
 
 
+def test_lightning_long_spans_ragged():
+    """The 128K batch at a token count that is not a multiple of a tile (nor
+    of a workgroup's span), so the scan runs its long spans and the last
+    workgroup of every request its ragged wave, with ragged valid lengths."""
+    n = 131072 - 37
+    seq = tuple([n, n - 1, 129999, 70001] + [n - 5 * i for i in range(4, 32)])
+    w = synth.get("lightning_128k").with_(name="lightning_128k_ragged", n=n, seq_lens=seq,
+                                          seed=1012)
+    print(f"[full] {w.name} n={n}", flush=True)
+    inp = synth.make_inputs(w, "cuda")
+    r = StepRunner(inp)
+    r.run()
+    torch.cuda.synchronize()
+    gsel = r.topk.cpu().numpy()
+    _check_rows(gsel, w)
+    scores = r.index_scores().cpu().numpy()
+    _check_lightning_sample(w, inp, r, scores, gsel, (0, 1, 3))
+    _rerun_identical(r)
+
+
 def test_block_sparse_80k_full():
     w = synth.get("block_sparse_80k")
     print(f"[full] {w.name}", flush=True)
