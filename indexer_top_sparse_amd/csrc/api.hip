@@ -324,11 +324,6 @@ int run_scores(const sparse_index_args& a, const IndexLayout& L, float* scores, 
   sp.scores = scores;
   sp.hist = hist;
   sp.n_units = L.n_units;
-  sp.depth = nullptr;
-  sp.plist = nullptr;
-  sp.pwl = nullptr;
-  sp.npl = nullptr;
-  sp.score_c = nullptr;
   switch (a.kind) {
     case SPARSE_SCORE_DOT:
       HIPCHECK(sd::launch_score_dot(sp, s));
@@ -448,9 +443,8 @@ int sparse_read_depth(const sparse_index_args* ia, int8_t* depth_out, void* stre
   if (ia->batch == 0) return SPARSE_OK;
   CHECK(depth_out, SPARSE_EINVAL, "depth_out NULL");
   CHECK(ia->q, SPARSE_EINVAL, "q NULL");
-  // the scan weights are a by-product the kernel skips when given NULL
   hipStream_t s = (hipStream_t)stream;
-  HIPCHECK(sd::launch_read_depth(ia, depth_out, nullptr, nullptr, nullptr, nullptr, s));
+  HIPCHECK(sd::launch_read_depth(ia, depth_out, s));
   return SPARSE_OK;
 }
 

@@ -210,11 +210,6 @@ struct ScorePlan {
   float* scores;     // [B][R][n_units]
   uint32_t* hist;    // [B*R][score_hist_parts][kHistWords] (nullable)
   int n_units;
-  int8_t* depth;     // BITPLANE: [B][Hkv][D]
-  int32_t* plist;    // BITPLANE: [B][Hkv][4D] read planes (index 4c + j), then
-  float* pwl;        //   their weights q_bar_c * cell_c * 2^(3-j)
-  int32_t* npl;      //   [B][Hkv] number of read planes
-  float* score_c;    // BITPLANE: [B][Hkv] constant term
 };
 // Histogram parts per row that the score kernel of `a` writes, and the
 // units each covers (0 when a part is not one contiguous span).
@@ -222,8 +217,7 @@ int score_hist_parts(const sparse_index_args& a);
 int score_part_span(const sparse_index_args& a);
 hipError_t launch_score_dot(const ScorePlan& p, hipStream_t s);
 hipError_t launch_score_lightning(const ScorePlan& p, hipStream_t s);
-hipError_t launch_read_depth(const sparse_index_args* a, int8_t* depth, int32_t* plist,
-                             float* pwl, int32_t* npl, float* score_c, hipStream_t s);
+hipError_t launch_read_depth(const sparse_index_args* a, int8_t* depth, hipStream_t s);
 hipError_t launch_score_bitplane(const ScorePlan& p, hipStream_t s);
 
 struct AttnPlan {

@@ -501,18 +501,19 @@ hipError_t launch_score_lightning(const ScorePlan& p, hipStream_t s) {
 }
 
 // ========================================================================
-// Fathom read depth: one workgroup per (request, KV head), one thread per
-// (channel, plane) gain.  All arithmetic that decides the allocation is
-// float64 with a fixed operation order: q_bar = ((q_0 + q_1) + ...),
-// imp = (q_bar * q_bar) * var, gain = imp * 4^-j (an exact power-of-two
-// scaling); those are exact for bf16 queries and fp32 variances, so the
-// ranking (gain desc, channel asc, plane asc) is reproducible bit for bit.
-// The workgroup also turns the depths into the scan's plane weights
-// W_{c,j} = q_bar_c * cell_c * 2^(3-j) for read planes and the constant
-// sum_c q_bar_c * (zero_c + cell_c * 2^(3 - t_c)).
+// Fathom read depth: the selection of one (request, KV head) in one
+// workgroup, one thread per (channel, plane) gain.  All arithmetic that
+// decides the allocation is float64 with a fixed operation order: q_bar =
+// ((q_0 + q_1) + ...), imp = (q_bar * q_bar) * var, gain = imp * 4^-j (an
+// exact power-of-two scaling); those are exact for bf16 queries and fp32
+// variances, so the ranking (gain desc, channel asc, plane asc) is
+// reproducible bit for bit.  read_depth_kernel (sparse_read_depth) writes
+// the depths t_c; the bit-plane scan makes the same selection in its
+// prologue and turns it into the plane weights W_{c,j} = q_bar_c * cell_c *
+// 2^(3-j) of the read planes and the constant sum_c q_bar_c * (zero_c +
+// cell_c * 2^(3 - t_c)).
 // ========================================================================
 constexpr int kDepthThreads = 512;  // D = 128 channels x 4 planes
-constexpr int kPlaneBatch = 8;      // plane-list entries the scan fetches at once
 
 // LDS of the read-depth selection of one (request, KV head).
 struct DepthLds {
@@ -664,61 +665,17 @@ __device__ __forceinline__ void depth_constant(DepthLds& L, int D) {
   }
 }
 
-// ========================================================================
-// Fathom read depth: one workgroup per (request, KV head), one thread per
-// (channel, plane) gain.  All arithmetic that decides the allocation is
-// float64 with a fixed operation order: q_bar = ((q_0 + q_1) + ...),
-// imp = (q_bar * q_bar) * var, gain = imp * 4^-j (an exact power-of-two
-// scaling); those are exact for bf16 queries and fp32 variances, so the
-// ranking (gain desc, channel asc, plane asc) is reproducible bit for bit.
-// The workgroup also turns the depths into the scan's plane weights
-// W_{c,j} = q_bar_c * cell_c * 2^(3-j) for read planes and the constant
-// sum_c q_bar_c * (zero_c + cell_c * 2^(3 - t_c)).  The fused step's scan
-// does the same work in its own prologue (score_bitplane_kernel); this
-// kernel serves sparse_read_depth.
-// ========================================================================
-__global__ __launch_bounds__(kDepthThreads) void read_depth_kernel(
-    sparse_index_args a, int8_t* __restrict__ depth, int32_t* __restrict__ plist,
-    float* __restrict__ pwl, int32_t* __restrict__ npl, float* __restrict__ score_c) {
+// The depths alone (sparse_read_depth): one workgroup per (request, KV head).
+__global__ __launch_bounds__(kDepthThreads) void read_depth_kernel(sparse_index_args a,
+                                                                   int8_t* __restrict__ depth) {
   __shared__ DepthLds L;
-  const int h = blockIdx.x;
-  const int b = blockIdx.y;
-  const int D = a.head_dim;
-  const int Hkv = a.n_kv_heads;
-  const int tid = threadIdx.x;
-  const int c = tid >> 2;
-  const int j = tid & 3;
-  const int64_t hd = ((int64_t)b * Hkv + h) * D;
   float cell_c;
-  depth_select<kDepthThreads>(a, b, h, L, cell_c, depth);
-  const int taken = c < D ? L.taken[tid] : 0;
-  if (plist) {
-    // read planes in (channel, plane) order with the weight of their bit
-    int total;
-    const int incl = block_inclusive_scan<kDepthThreads>(taken, L.scan, &total);
-    if (taken) {
-      const double qb = L.qbar[c];
-      plist[hd * 4 + incl - 1] = tid;
-      pwl[hd * 4 + incl - 1] = (float)(qb * (double)cell_c * ldexp(1.0, 3 - j));
-    }
-    if (tid == 0) npl[(int64_t)b * Hkv + h] = total;
-    // pad the list to a multiple of kPlaneBatch with weightless plane 0
-    const int padded = (total + kPlaneBatch - 1) / kPlaneBatch * kPlaneBatch;
-    if (tid >= total && tid < padded) {
-      plist[hd * 4 + tid] = 0;
-      pwl[hd * 4 + tid] = 0.f;
-    }
-  }
-  if (score_c) {
-    depth_constant(L, D);
-    if (tid == 0) score_c[(int64_t)b * Hkv + h] = (float)L.cterm[0];
-  }
+  depth_select<kDepthThreads>(a, blockIdx.y, blockIdx.x, L, cell_c, depth);
 }
 
-hipError_t launch_read_depth(const sparse_index_args* a, int8_t* depth, int32_t* plist,
-                             float* pwl, int32_t* npl, float* score_c, hipStream_t s) {
+hipError_t launch_read_depth(const sparse_index_args* a, int8_t* depth, hipStream_t s) {
   dim3 grid(a->n_kv_heads, a->batch);
-  read_depth_kernel<<<grid, kDepthThreads, 0, s>>>(*a, depth, plist, pwl, npl, score_c);
+  read_depth_kernel<<<grid, kDepthThreads, 0, s>>>(*a, depth);
   return hipGetLastError();
 }
 
@@ -727,9 +684,9 @@ hipError_t launch_read_depth(const sparse_index_args* a, int8_t* depth, int32_t*
 // (request, KV head): 32 consecutive tokens.  The workgroup first selects
 // the read depths itself (depth_select, the same selection as
 // read_depth_kernel, repeated by every workgroup of the (request, KV head):
-// cheaper than a launch of its own); a plane list written by
-// read_depth_kernel can be passed instead.  The read planes (c, j) are
-// taken six at a time.  For each group
+// cheaper than a launch of its own) and turns them into the list of read
+// planes (c, j) with their weights and the score constant.  The read planes
+// are taken six at a time.  For each group
 // of six the workgroup tabulates the 64 sums of their weights W_{c,j} over
 // every subset; a thread loads the six plane words (buffer loads, coalesced
 // across the workgroup), transposes the 8 x 8 bit blocks of two zero words
@@ -799,8 +756,7 @@ static_assert(sizeof(DepthLds) <= kBpLdsBytes - kBpLdsStage && kBpLdsStage % 8 =
               "the read-depth selection fits the staging LDS");
 
 __global__ __launch_bounds__(kBpThreads) void score_bitplane_kernel(
-    sparse_index_args a, const int32_t* plist, const float* pwl, const int32_t* npl,
-    const float* score_c, float* __restrict__ scores, uint32_t* hist, int n_units) {
+    sparse_index_args a, float* __restrict__ scores, uint32_t* hist, int n_units) {
   __shared__ __attribute__((aligned(16))) char lds[kBpLdsBytes];
   float* lut_s = (float*)(lds + kBpLdsLut);
   uint32_t* poff_s = (uint32_t*)(lds + kBpLdsPoff);  // byte offset of each read plane
@@ -818,17 +774,7 @@ __global__ __launch_bounds__(kBpThreads) void score_bitplane_kernel(
   // a plane's byte offset fits 32 bits
   int np;
   float c0;
-  if (plist) {
-    // the plane list read_depth_kernel wrote
-    np = npl[bh];
-    for (int i = threadIdx.x; i < np; i += kBpThreads) {
-      poff_s[i] = (uint32_t)plist[bh * 4 * D + i] * (uint32_t)nw * 4u;
-      pw_s[i] = pwl[bh * 4 * D + i];
-    }
-    if (hist) lh.clear(kBpThreads);  // (ends with a barrier)
-    else __syncthreads();
-    c0 = score_c[bh];
-  } else {
+  {
     // the read depth computed here, in the LDS the score staging uses later:
     // every workgroup of the (request, KV head) repeats the same selection,
     // which costs less than a launch of its own
@@ -962,8 +908,7 @@ __global__ __launch_bounds__(kBpThreads) void score_bitplane_kernel(
 hipError_t launch_score_bitplane(const ScorePlan& p, hipStream_t s) {
   const sparse_index_args& a = *p.a;
   dim3 grid(bitplane_parts(a), a.n_kv_heads, a.batch);
-  score_bitplane_kernel<<<grid, kBpThreads, 0, s>>>(a, p.plist, p.pwl, p.npl, p.score_c,
-                                                   p.scores, p.hist, p.n_units);
+  score_bitplane_kernel<<<grid, kBpThreads, 0, s>>>(a, p.scores, p.hist, p.n_units);
   return hipGetLastError();
 }
 
