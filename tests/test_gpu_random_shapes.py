@@ -63,7 +63,30 @@ def _shapes():
     return out
 
 
-SHAPES = _shapes()
+def _edges():
+    """Boundary shapes: one tile plus one token, a span plus one, k at or above
+    the valid units, a single block or word, rows just past the select-only
+    size."""
+    L = synth.get("lightning_small")
+    Bk = synth.get("block_sparse_small")
+    T = synth.get("tiny_fp32_small")
+    F = synth.get("fathom_small")
+    return [
+        L.with_(name="edge_lightning_33", B=5, n=33, k=32, seq_lens=(33, 1, 32, 17, 33),
+                page=64, seed=3501),
+        L.with_(name="edge_lightning_span1", B=2, n=8193, k=8193, seq_lens=(8193, 4097),
+                page=0, seed=3502),
+        Bk.with_(name="edge_block_one", B=2, n=64, k=4, seq_lens=(64, 5), seed=3503),
+        Bk.with_(name="edge_block_129", B=3, n=129, k=3, seq_lens=(129, 128, 65), seed=3504),
+        T.with_(name="edge_dot_one", B=2, n=1, k=1, seq_lens=(1, 1), seed=3505),
+        T.with_(name="edge_dot_12289", B=2, n=12289, k=600, seq_lens=(12289, 12288), seed=3506),
+        F.with_(name="edge_fathom_31", B=2, n=31, k=5, budget=92, seq_lens=(31, 3), seed=3507),
+        F.with_(name="edge_fathom_32769", B=1, n=32769, k=2048, budget=300, seq_lens=(32769,),
+                seed=3508),
+    ]
+
+
+SHAPES = _shapes() + _edges()
 
 
 @pytest.mark.parametrize("w", SHAPES, ids=[w.name for w in SHAPES])
