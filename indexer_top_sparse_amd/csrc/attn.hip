@@ -929,7 +929,8 @@ __global__ __launch_bounds__(512) void attn_combine_mla_kernel(AttnPlan p) {
       mv[u] = ps[kMlaHeadsWG * 512 + 2 * hl];
       lv[u] = s0 + u < S ? ps[kMlaHeadsWG * 512 + 2 * hl + 1] : 0.f;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) pv[u][j] = *(const f32x4*)(ps + ((slot + j) * 64 + lane) * 4);
+      for (int j = 0; j < 4; ++j)  // each record is read once: non-temporal
+        pv[u][j] = __builtin_nontemporal_load((const f32x4*)(ps + ((slot + j) * 64 + lane) * 4));
     }
     float mb = M;
 #pragma unroll
