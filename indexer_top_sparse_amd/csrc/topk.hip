@@ -284,7 +284,8 @@ __global__ __launch_bounds__(NT) void topk_filter_fused_kernel(TopkPlan p) {
     if (u0 + kFfPer <= hi && ((uintptr_t)(row + u0) & 15u) == 0) {
 #pragma unroll
       for (int i = 0; i < kFfPer; i += 4) {
-        const f32x4 x = *(const f32x4*)(row + u0 + i);
+        // scores are read once here: non-temporal
+        const f32x4 x = __builtin_nontemporal_load((const f32x4*)(row + u0 + i));
 #pragma unroll
         for (int e = 0; e < 4; ++e) raw[i + e] = x[e];
       }
@@ -498,8 +499,8 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkPlan p) {
 #pragma unroll
     for (int j = 0; j < kSelSpec; ++j) {
       const int q = tid + j * kSelThreads;
-      skey[j] = q < p.n_units ? ck0[q] : 0u;
-      sidx[j] = q < p.n_units ? ci0[q] : 0;
+      skey[j] = q < p.n_units ? __builtin_nontemporal_load(ck0 + q) : 0u;
+      sidx[j] = q < p.n_units ? __builtin_nontemporal_load(ci0 + q) : 0;
     }
     M = min((int)p.cand_total[r], p.n_units);
     __syncthreads();
