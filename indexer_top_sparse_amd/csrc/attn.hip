@@ -600,6 +600,9 @@ struct GqaTile {
 
 // (At most 256 VGPRs, so that two workgroups share a compute unit: at 260
 // the kernel ran one workgroup per unit.)
+// NT: the K/V rows are loaded non-temporally (chosen by the launch when the
+// step gathers more than the last-level cache could keep for the next step).
+template <bool NT>
 __global__ __launch_bounds__(64 * kGqaWaves, 2) void attn_gqa_kernel(AttnPlan p) {
   __shared__ __attribute__((aligned(16))) uint16_t vs_s[kGqaWaves][kTT * kGqaRowV];
   __shared__ uint64_t rowp_s[kMaxSplitTok];
@@ -665,13 +668,17 @@ __global__ __launch_bounds__(64 * kGqaWaves, 2) void attn_gqa_kernel(AttnPlan p)
     for (int mt = 0; mt < 2; ++mt) {
       const char* kr = (const char*)rowp_s[tile * kTT + 16 * mt + n] + 16 * g;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) T.k[mt][s] = *(gptr<const u32x4>)(kr + 64 * s);
+      for (int s = 0; s < 4; ++s) {
+        gptr<const u32x4> ka = (gptr<const u32x4>)(kr + 64 * s);
+        T.k[mt][s] = NT ? __builtin_nontemporal_load(ka) : *ka;
+      }
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const uint64_t kp = rowp_s[tile * kTT + g + 4 * u];
       const char* vp = kp == dummy ? (const char*)kp : (const char*)kp + vdelta;
-      T.v[u] = *(gptr<const u32x4>)(vp + 16 * n);
+      gptr<const u32x4> va = (gptr<const u32x4>)(vp + 16 * n);
+      T.v[u] = NT ? __builtin_nontemporal_load(va) : *va;
     }
   };
 
@@ -834,7 +841,17 @@ hipError_t launch_attn_bf16(const AttnPlan& p, hipStream_t s) {
   } else if (a.d_qk == 128 && a.d_v == 128 && a.v_cache != nullptr) {
     const int groups = a.n_kv_heads;
     dim3 grid((unsigned)(8 * groups * rounds), 1, 1);
-    attn_gqa_kernel<<<grid, 64 * kGqaWaves, 0, s>>>(p);
+    // K and V rows gathered by this launch; from a quarter of the 256 MB
+    // last-level cache up they would not stay there for the next step (the
+    // other layers and the index stream pass through it too), so they stream
+    // (block_sparse_80k, 128 MiB per layer: 7708 -> 7846 steps/s); smaller
+    // gathers stay cacheable for the overlapping selection of the next step
+    // (fathom_1m, 8 MiB: non-temporal loads measured 13890 -> 13583)
+    const int64_t gathered = (int64_t)a.batch * p.k_tokens * a.n_kv_heads * (a.d_qk + a.d_v) * 2;
+    if (gathered >= ((int64_t)64 << 20))
+      attn_gqa_kernel<true><<<grid, 64 * kGqaWaves, 0, s>>>(p);
+    else
+      attn_gqa_kernel<false><<<grid, 64 * kGqaWaves, 0, s>>>(p);
   } else {
     return hipErrorInvalidValue;
   }
