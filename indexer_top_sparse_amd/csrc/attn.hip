@@ -542,9 +542,13 @@ __global__ __launch_bounds__(kMlaThreads, 1) void attn_mla_kernel(AttnPlan p) {
     if (ntiles > 0) {
       __syncthreads();
       for (int t = 0; t < ntiles; ++t) {
+        // the P V MFMAs first: the score waves commit and gather while
+        // these issue, and the P V waves commit and gather while the score
+        // MFMAs issue (lightning_128k 6178 -> 6200-6211 steps/s, hot_16k
+        // without misses 2706 -> 2748 against committing first)
+        pv(t % 3, t & 1);
         commit(pre, (t + 2) % 3);
         gather(pre, t + 3);
-        pv(t % 3, t & 1);
         __syncthreads();
       }
     }
