@@ -297,7 +297,9 @@ sd::TopkPlan make_topk_plan(const IndexLayout& L, char* ws, const float* scores,
   return p;
 }
 
-int run_topk(const sd::TopkPlan& p, bool hist_ready, hipStream_t s) {
+// with_select false: the latent attention makes the selection from the
+// fused filter's candidates itself (the fused step only).
+int run_topk(const sd::TopkPlan& p, bool hist_ready, hipStream_t s, bool with_select = true) {
   if (p.rows == 0) return SPARSE_OK;
   if (p.n_units == 0) {
     // nothing valid: the select kernel only pads
@@ -313,7 +315,7 @@ int run_topk(const sd::TopkPlan& p, bool hist_ready, hipStream_t s) {
       HIPCHECK(sd::launch_topk_filter(p, s));
     }
   }
-  HIPCHECK(sd::launch_topk_select(p, s));
+  if (with_select) HIPCHECK(sd::launch_topk_select(p, s));
   return SPARSE_OK;
 }
 
@@ -339,11 +341,14 @@ int run_scores(const sparse_index_args& a, const IndexLayout& L, float* scores, 
   return SPARSE_OK;
 }
 
+// fused_tp: the fused filter's candidates, from which the attention selects
+// (attn_selects) and writes the selection to sel_out; NULL: sel holds it.
 int run_attn(const sparse_attn_args& a, const int32_t* sel, int sel_heads, int k,
-             int sel_unit, float* out, float* lse, char* ws, size_t base, hipStream_t s) {
+             int sel_unit, float* out, float* lse, char* ws, size_t base, hipStream_t s,
+             const sd::TopkPlan* fused_tp = nullptr, int32_t* sel_out = nullptr) {
   const int k_tokens = k * sel_unit;
   AttnLayout L = attn_layout(a, k_tokens, base);
-  sd::AttnPlan p;
+  sd::AttnPlan p{};
   p.a = a;
   p.sel = sel;
   p.sel_heads = sel_heads;
@@ -355,6 +360,9 @@ int run_attn(const sparse_attn_args& a, const int32_t* sel, int sel_heads, int k
   p.part = L.splits > 1 ? (float*)(ws + L.part) : nullptr;
   p.staging = a.hot_slot ? (uint16_t*)(ws + L.staging) : nullptr;
   p.k_tokens = k_tokens;
+  p.fsel = fused_tp != nullptr;
+  p.sel_out = sel_out;
+  if (fused_tp) p.tk = *fused_tp;
   if (a.hot_slot) HIPCHECK(sd::launch_miss_fetch(p, s));
   if (a.dtype == SPARSE_F32) HIPCHECK(sd::launch_attn_f32(p, s));
   else HIPCHECK(sd::launch_attn_bf16(p, s));
@@ -523,9 +531,16 @@ int sparse_decode_step(const sparse_index_args* ia, const sparse_attn_args* aa, 
     rc = run_scores(*ia, L, scores, tp.direct ? nullptr : tp.hist, s);
     if (rc) return rc;
   }
-  rc = run_topk(tp, true, s);
+  // Latent rows without a hot buffer: the attention selects from the fused
+  // filter's candidates in its prologue and writes topk_out itself, instead
+  // of a select launch whose output it would read back (lightning_128k:
+  // see the latent attention's row table).
+  const bool fsel = tp.fused && !tp.direct && tp.n_units > 0 && sel_heads == 1 &&
+                    unit == 1 && sd::attn_selects(*aa);
+  rc = run_topk(tp, true, s, !fsel);
   if (rc) return rc;
-  return run_attn(*aa, topk_out, sel_heads, k, unit, out, lse, w, L.end, s);
+  return run_attn(*aa, topk_out, sel_heads, k, unit, out, lse, w, L.end, s,
+                  fsel ? &tp : nullptr, topk_out);
 }
 
 int sparse_decode_step_noalloc(const sparse_index_args* ia, const sparse_attn_args* aa,

@@ -12,7 +12,7 @@
 // keeps per-head running max and sum; P V runs on the same MFMA with V read
 // from LDS as 8-token column strips re-packed in registers.  Splits write
 // unnormalised partials that a combine kernel merges by log-sum-exp.
-#include "common.hpp"
+#include "select.hpp"
 
 namespace sd {
 
@@ -296,6 +296,9 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const uint16_t* p) {
       (__attribute__((address_space(3))) s16x4*)(uint16_t*)p);
 }
 
+// FSEL: the fused step's selection is made here (see the row table below).
+constexpr int kMlaSelCap = 11264;  // candidates of the fused selection staged in LDS
+template <bool FSEL>
 __global__ __launch_bounds__(kMlaThreads, 1) void attn_mla_kernel(AttnPlan p) {
   __shared__ __attribute__((aligned(16))) uint16_t ks_s[3][kTT * kMlaRow];
   // probabilities of a tile as the P V waves' B operands, [buffer][head block][lane]
@@ -330,6 +333,35 @@ __global__ __launch_bounds__(kMlaThreads, 1) void attn_mla_kernel(AttnPlan p) {
   const int64_t stage_base = (int64_t)b * p.sel_heads * p.k_tokens;
   RowAddr ra{A};
 
+  if constexpr (FSEL) {
+    // The fused step's top-k of request b, from the fused filter's candidate
+    // list: every workgroup of the request selects the whole row (the tile
+    // buffers, unused until the first gather, hold the select's LDS) and
+    // keeps the tokens of its split's positions in rowp_s, which the row
+    // table below turns into row addresses in place; head group 0 writes the
+    // split's positions of the caller's top-k buffer.  This takes the place
+    // of the select kernel and of the round trip through that buffer.
+    static_assert(sizeof(SelectLds<kMlaThreads, kMlaSelCap>) <= sizeof(ks_s),
+                  "the select's LDS fits in the tile buffers");
+    auto& SL = *reinterpret_cast<SelectLds<kMlaThreads, kMlaSelCap>*>(&ks_s[0][0]);
+    int32_t* so = p.sel_out + (int64_t)b * p.k;
+    select_row<kMlaThreads, kMlaSelCap, 8>(
+        p.tk, b, SL,
+        [&](int pos, int32_t unit_idx, uint32_t) {
+          if (pos >= j0 && pos < j1) {
+            rowp_s[pos - j0] = (uint64_t)(uint32_t)unit_idx;
+            if (grp == 0) so[pos] = unit_idx;
+          }
+        },
+        [&](int pos) {
+          if (pos >= j0 && pos < j1) {
+            rowp_s[pos - j0] = ~0ull;
+            if (grp == 0) so[pos] = -1;
+          }
+        });
+    __syncthreads();
+  }
+
   // Row table: the K row address of every split position (masked positions
   // and the prefetch pad point at the library's zero row, so every load in
   // the pipeline is unconditional) and, per 32-token tile, the valid-token
@@ -339,7 +371,12 @@ __global__ __launch_bounds__(kMlaThreads, 1) void attn_mla_kernel(AttnPlan p) {
     const int i = base + tid;
     int t = -1;
     if (i < cnt) {
-      t = sel_token(selrow, j0 + i, p.sel_unit, valid);
+      if constexpr (FSEL) {
+        t = (int32_t)(uint32_t)rowp_s[i];  // the selected token, or -1
+        if (t >= valid) t = -1;
+      } else {
+        t = sel_token(selrow, j0 + i, p.sel_unit, valid);
+      }
       rowp_s[i] = t >= 0 ? (uint64_t)ra.k_row(b, 0, t, stage_base + j0 + i, p.staging, 2)
                          : dummy;
     }
@@ -833,6 +870,10 @@ __global__ __launch_bounds__(64 * kGqaWaves, 2) void attn_gqa_kernel(AttnPlan p)
   }
 }
 
+bool attn_selects(const sparse_attn_args& a) {
+  return a.dtype == SPARSE_BF16 && mla_shape(a) && a.hot_slot == nullptr;
+}
+
 hipError_t launch_attn_bf16(const AttnPlan& p, hipStream_t s) {
   const sparse_attn_args& a = p.a;
   // 8 * groups * ceil(units / 8) workgroup ids (the kernel decodes them)
@@ -841,7 +882,8 @@ hipError_t launch_attn_bf16(const AttnPlan& p, hipStream_t s) {
   if (mla_shape(a)) {
     const int groups = a.n_q_heads / kMlaHeadsWG;
     dim3 grid((unsigned)(8 * groups * rounds), 1, 1);
-    attn_mla_kernel<<<grid, kMlaThreads, 0, s>>>(p);
+    if (p.fsel) attn_mla_kernel<true><<<grid, kMlaThreads, 0, s>>>(p);
+    else attn_mla_kernel<false><<<grid, kMlaThreads, 0, s>>>(p);
   } else if (a.d_qk == 128 && a.d_v == 128 && a.v_cache != nullptr) {
     const int groups = a.n_kv_heads;
     dim3 grid((unsigned)(8 * groups * rounds), 1, 1);

@@ -232,7 +232,16 @@ struct AttnPlan {
   // hot buffer: staging of fetched rows [B][k_tokens][d_qk] bf16
   uint16_t* staging;
   int k_tokens;       // selected tokens per (request, sel row)
+  // fused step, latent rows (attn_selects): the attention selects each
+  // request's top-k itself from the fused filter's candidates (tk) and
+  // writes the selection to sel_out [B][k]; sel is then unused
+  int fsel;
+  int32_t* sel_out;
+  TopkPlan tk;
 };
+// Whether the attention over these arguments can take the selection from the
+// fused filter's candidates itself (latent rows, no hot buffer).
+bool attn_selects(const sparse_attn_args& a);
 hipError_t launch_attn_f32(const AttnPlan& p, hipStream_t s);
 hipError_t launch_attn_bf16(const AttnPlan& p, hipStream_t s);
 hipError_t launch_attn_combine(const AttnPlan& p, hipStream_t s);

@@ -32,19 +32,9 @@
 //           k-th key T and how many units equal to T are needed, then
 //           writes the selection in index order with block prefix sums
 //           (ties to the lowest indices).
-#include "common.hpp"
+#include "select.hpp"
 
 namespace sd {
-
-__device__ __forceinline__ int row_valid_units(const TopkPlan& p, int r) {
-  int v = p.n_units;
-  if (p.valid) {
-    int t = p.valid[r / p.rows_per_valid];
-    if (p.unit_div > 1) t = (t + p.unit_div - 1) / p.unit_div;
-    v = t < 0 ? 0 : (t > p.n_units ? p.n_units : t);
-  }
-  return v;
-}
 
 // --------------------------------------------------------------------- hist
 // Part c of row r's histogram: the valid units of chunk c (p.parts must be
@@ -69,37 +59,6 @@ hipError_t launch_topk_hist(const TopkPlan& p, hipStream_t s) {
   dim3 grid(p.n_chunks, p.rows);
   topk_hist_kernel<<<grid, 256, 0, s>>>(p);
   return hipGetLastError();
-}
-
-// Find, over `nbins` LDS bins counted from the top, the bin holding the
-// need-th largest key: out[0] = bin, out[1] = units in higher bins.
-template <int NT>
-__device__ void find_bin_from_top(const uint32_t* hist, int nbins, int need,
-                                  int* scan_lds, int* out) {
-  const int per = nbins / NT > 0 ? nbins / NT : 1;
-  const int t = threadIdx.x;
-  const bool owns = per * t < nbins;
-  const int top = nbins - 1 - per * t;
-  int local = 0;
-  if (owns)
-    for (int i = 0; i < per; ++i) local += (int)hist[top - i];
-  int total;
-  int incl = block_inclusive_scan<NT>(local, scan_lds, &total);
-  int excl = incl - local;
-  if (owns && excl < need && incl >= need) {
-    int cum = excl;
-    for (int i = 0; i < per; ++i) {
-      int b = top - i;
-      int c = (int)hist[b];
-      if (cum + c >= need) {
-        out[0] = b;
-        out[1] = cum;
-        break;
-      }
-      cum += c;
-    }
-  }
-  __syncthreads();
 }
 
 // --------------------------------------------------------------------- bin
@@ -424,231 +383,23 @@ constexpr int kSelThreads = 1024;
 constexpr int kSelCap = 12288;  // candidates staged in LDS (96 KB)
 static_assert(kTopkDirectMax <= kSelCap, "a direct row fits in LDS");
 
-__device__ __forceinline__ int find_chunk(const int* excl, int nchunks, int p) {
-  // largest c with excl[c] <= p
-  int lo = 0, hi = nchunks - 1;
-  while (lo < hi) {
-    int mid = (lo + hi + 1) >> 1;
-    if (excl[mid] <= p) lo = mid; else hi = mid - 1;
-  }
-  return lo;
-}
-
+// One workgroup per row (select_row); the fused filter's first 4 x 1024
+// list entries are loaded together with the count.
 __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkPlan p) {
-  __shared__ uint32_t ckey_s[kSelCap];
-  __shared__ int32_t cidx_s[kSelCap];
-  __shared__ uint32_t hs[kHistBins];
-  __shared__ int excl[1025];
-  __shared__ int scan_lds[kSelThreads / 64 + 1];
-  __shared__ int res[2];
+  __shared__ SelectLds<kSelThreads, kSelCap> L;
   const int r = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int v = row_valid_units(p, r);
-  const int k_eff = min(p.k, v);
   int32_t* oi = p.idx_out + (int64_t)r * p.k;
   float* ov = p.val_out ? p.val_out + (int64_t)r * p.k : nullptr;
-  for (int j = k_eff + tid; j < p.k; j += kSelThreads) {
-    oi[j] = -1;
-    if (ov) ov[j] = -__builtin_huge_valf();
-  }
-  if (k_eff <= 0) return;
-
-  uint32_t b1;
-  int above;
-  const int wid = tid >> 6;
-  const int lane = tid & 63;
-
-  // level-2 histogram (bits [19:8] of the keys in bin b1), counted while
-  // the candidates are staged
-  for (int i = tid; i < kHistBins; i += kSelThreads) hs[i] = 0u;
-  // candidate count and (per-chunk slices) chunk offsets.  The fused
-  // filter's list starts at the row base, so its first kSelSpec * kSelThreads
-  // entries are loaded together with the count (one round trip).
-  constexpr int kSelSpec = 4;
-  uint32_t skey[kSelSpec];
-  int32_t sidx[kSelSpec];
-  int M = 0;
-  if (p.direct) {
-    // the row is the candidate list: every valid unit, in index order; its
-    // top 12 key bits give b* and the count above it
-    M = v;
-    const float* sr = p.scores + (int64_t)r * p.row_stride;
-    __syncthreads();  // hs cleared
-    for (int q = tid; q < M; q += kSelThreads) {
-      const uint32_t key = score_key(sr[q]);
-      ckey_s[q] = key;
-      cidx_s[q] = q;
-      atomicAdd(&hs[key >> 20], 1u);
-    }
-    if (tid == 0) { res[0] = 0; res[1] = 0; }
-    __syncthreads();
-    find_bin_from_top<kSelThreads>(hs, kHistBins, k_eff, scan_lds, res);
-    b1 = (uint32_t)res[0];
-    above = res[1];
-    for (int i = tid; i < kHistBins; i += kSelThreads) hs[i] = 0u;
-    __syncthreads();
-    for (int q = tid; q < M; q += kSelThreads) {
-      const uint32_t key = ckey_s[q];
-      if ((key >> 20) == b1) atomicAdd(&hs[(key >> 8) & 0xFFFu], 1u);
-    }
-  } else if (p.fused) {
-    b1 = p.bstar[2 * r];
-    above = (int)p.bstar[2 * r + 1];
-    const uint32_t* ck0 = p.cand_key + (int64_t)r * p.n_units;
-    const int32_t* ci0 = p.cand_idx + (int64_t)r * p.n_units;
-#pragma unroll
-    for (int j = 0; j < kSelSpec; ++j) {
-      const int q = tid + j * kSelThreads;
-      skey[j] = q < p.n_units ? __builtin_nontemporal_load(ck0 + q) : 0u;
-      sidx[j] = q < p.n_units ? __builtin_nontemporal_load(ci0 + q) : 0;
-    }
-    M = min((int)p.cand_total[r], p.n_units);
-    __syncthreads();
-  } else {
-    b1 = p.bstar[2 * r];
-    above = (int)p.bstar[2 * r + 1];
-    const uint32_t* cc = p.chunk_cnt + (int64_t)r * p.n_chunks;
-    for (int base = 0; base < p.n_chunks; base += kSelThreads) {
-      int c = base + tid;
-      int x = c < p.n_chunks ? (int)cc[c] : 0;
-      int total;
-      int incl = block_inclusive_scan<kSelThreads>(x, scan_lds, &total);
-      if (c < p.n_chunks) excl[c] = M + incl - x;
-      M += total;
-      __syncthreads();
-    }
-  }
-  const uint32_t* ck = p.cand_key + (int64_t)r * p.n_units;
-  const int32_t* ci = p.cand_idx + (int64_t)r * p.n_units;
-  const int nch = p.n_chunks;
-  auto cand_off = [&](int q) -> int64_t {
-    if (p.fused) return q;
-    int c = find_chunk(excl, nch, q);
-    return (int64_t)c * kTopkChunk + (q - excl[c]);
-  };
-  // stage the candidates (in index order) in LDS when they fit: the fused
-  // filter's single list by all threads, per-chunk slices by wave w copying
-  // chunks w, w + 16, ...
-  const bool inlds = p.direct || M <= kSelCap;
-  if (p.direct) {
-    // staged and counted above
-  } else if (inlds && p.fused) {
-#pragma unroll
-    for (int j = 0; j < kSelSpec; ++j) {
-      const int q = tid + j * kSelThreads;
-      if (q < M) {
-        ckey_s[q] = skey[j];
-        cidx_s[q] = sidx[j];
-        if ((skey[j] >> 20) == b1) atomicAdd(&hs[(skey[j] >> 8) & 0xFFFu], 1u);
-      }
-    }
-    for (int q = tid + kSelSpec * kSelThreads; q < M; q += kSelThreads) {
-      const uint32_t key = ck[q];
-      ckey_s[q] = key;
-      cidx_s[q] = ci[q];
-      if ((key >> 20) == b1) atomicAdd(&hs[(key >> 8) & 0xFFFu], 1u);
-    }
-  } else if (inlds) {
-    for (int c = wid; c < nch; c += kSelThreads / 64) {
-      const int cnt = (c + 1 < nch ? excl[c + 1] : M) - excl[c];
-      const int dst = excl[c];
-      for (int i = lane; i < cnt; i += 64) {
-        const uint32_t key = ck[(int64_t)c * kTopkChunk + i];
-        ckey_s[dst + i] = key;
-        cidx_s[dst + i] = ci[(int64_t)c * kTopkChunk + i];
-        if ((key >> 20) == b1) atomicAdd(&hs[(key >> 8) & 0xFFFu], 1u);
-      }
-    }
-  } else {
-    for (int q = tid; q < M; q += kSelThreads) {
-      const uint32_t key = ck[cand_off(q)];
-      if ((key >> 20) == b1) atomicAdd(&hs[(key >> 8) & 0xFFFu], 1u);
-    }
-  }
-  auto key_at = [&](int q) -> uint32_t { return inlds ? ckey_s[q] : ck[cand_off(q)]; };
-  auto idx_at = [&](int q) -> int32_t { return inlds ? cidx_s[q] : ci[cand_off(q)]; };
-  if (tid == 0) { res[0] = 0; res[1] = 0; }
-  __syncthreads();
-  find_bin_from_top<kSelThreads>(hs, kHistBins, k_eff - above, scan_lds, res);
-  const uint32_t b2 = (uint32_t)res[0];
-  above += res[1];
-  const uint32_t pre = (b1 << 12) | b2;
-  // When every key of the boundary 24-bit prefix is needed (the usual case),
-  // the prefix itself is the threshold and the last level is skipped.
-  const bool whole_prefix = (int)hs[b2] == k_eff - above;
-  __syncthreads();
-
-  uint32_t T;      // threshold on key >> shift
-  int shift;
-  int eq_need, eq_total;
-  if (whole_prefix) {
-    T = pre;
-    shift = 8;
-    eq_need = eq_total = k_eff - above;
-  } else {
-    // level 3: bits [7:0] of the keys with prefix (b1, b2)
-    for (int i = tid; i < 256; i += kSelThreads) hs[i] = 0u;
-    __syncthreads();
-    for (int q = tid; q < M; q += kSelThreads) {
-      uint32_t key = key_at(q);
-      if ((key >> 8) == pre) atomicAdd(&hs[key & 0xFFu], 1u);
-    }
-    if (tid == 0) { res[0] = 0; res[1] = 0; }
-    __syncthreads();
-    find_bin_from_top<kSelThreads>(hs, 256, k_eff - above, scan_lds, res);
-    const uint32_t d3 = (uint32_t)res[0];
-    T = (pre << 8) | d3;
-    shift = 0;
-    eq_need = k_eff - (above + res[1]);
-    eq_total = (int)hs[d3];
-    __syncthreads();
-  }
-
-  // final ordered pass, 4 consecutive candidates per thread per round
-  int eq_carry = 0, take_carry = 0;
-  const bool all_ties = (eq_total == eq_need);
-  for (int base = 0; base < M; base += 4 * kSelThreads) {
-    const int q0 = base + 4 * tid;
-    uint32_t key[4];
-    int gt[4], eq[4];
-    int n_eq = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int q = q0 + i;
-      key[i] = q < M ? key_at(q) : 0u;
-      gt[i] = (q < M) && (key[i] >> shift) > T;
-      eq[i] = (q < M) && (key[i] >> shift) == T;
-      n_eq += eq[i];
-    }
-    int take[4];
-    if (all_ties) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) take[i] = gt[i] | eq[i];
-    } else {
-      int total;
-      int incl = block_inclusive_scan<kSelThreads>(n_eq, scan_lds, &total);
-      int rank = eq_carry + incl - n_eq;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        take[i] = gt[i] || (eq[i] && rank < eq_need);
-        rank += eq[i];
-      }
-      eq_carry += total;
-    }
-    const int n_take = take[0] + take[1] + take[2] + take[3];
-    int total;
-    int incl = block_inclusive_scan<kSelThreads>(n_take, scan_lds, &total);
-    int pos = take_carry + incl - n_take;
-    take_carry += total;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (take[i] && pos < k_eff) {
-        oi[pos] = idx_at(q0 + i);
-        if (ov) ov[pos] = key_score(key[i]);
-        ++pos;
-      }
-    }
-  }
+  select_row<kSelThreads, kSelCap, 4>(
+      p, r, L,
+      [&](int pos, int32_t idx, uint32_t key) {
+        oi[pos] = idx;
+        if (ov) ov[pos] = key_score(key);
+      },
+      [&](int pos) {
+        oi[pos] = -1;
+        if (ov) ov[pos] = -__builtin_huge_valf();
+      });
 }
 
 hipError_t launch_topk_select(const TopkPlan& p, hipStream_t s) {

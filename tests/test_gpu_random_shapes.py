@@ -83,6 +83,14 @@ def _edges():
         F.with_(name="edge_fathom_31", B=2, n=31, k=5, budget=92, seq_lens=(31, 3), seed=3507),
         F.with_(name="edge_fathom_32769", B=1, n=32769, k=2048, budget=300, seq_lens=(32769,),
                 seed=3508),
+        # latent rows past the select-only size: the attention selects from
+        # the fused filter's candidates itself (one row shorter than k pads)
+        L.with_(name="edge_lightning_fused_12289", B=3, n=12289, k=2048,
+                seq_lens=(12289, 2000, 6001), page=64, seed=3509),
+        L.with_(name="edge_lightning_fused_40000", B=2, n=40000, k=300, hq=256,
+                seq_lens=(40000, 23457), page=0, seed=3510),
+        L.with_(name="edge_lightning_fused_k4096", B=2, n=30000, k=4096, hq=64,
+                seq_lens=(29999, 4097), page=64, seed=3511),
     ]
 
 
@@ -125,6 +133,9 @@ def test_random_step_matches_oracle(w):
     for row in range(rows):
         exp = O.topk(sc[row], w.k, valid_units(w, row // s.shape[1]))
         assert np.array_equal(gi[row], exp), ("topk", row)
+    # the step's own selection (select kernel, or the latent attention's fused
+    # select) is the same exact top-k of the same scores
+    assert np.array_equal(g.reshape(rows, -1), gi), "step selection"
     # attention over the GPU's own selection
     ref_g = oracle_step(w, arr, sel_in=g.astype(np.int64))
     outs = ref_g["layers"][0]["out"] if w.kind == "block" else ref_g["out"]
