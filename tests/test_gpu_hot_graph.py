@@ -6,7 +6,8 @@
   ("XM-Sparse" blog: fixed miss rates, misses fetched over PCIe into HBM).
 * A captured step replayed several times, with eager work and
   synchronisation in between, must reproduce the eager result bit for bit
-  on every replay.
+  on every replay (also for a latent step long enough that its attention
+  makes the top-k selection itself).
 """
 import numpy as np
 import pytest
@@ -66,9 +67,18 @@ def test_hot_step_matches_oracle_and_no_miss_run(hot_case):
     assert torch.equal(r_miss.lses[0], r_all.lses[0])
 
 
-@pytest.mark.parametrize("name", ["lightning_small", "block_sparse_small", "fathom_small"])
+def _graph_workload(name):
+    if name == "lightning_fused":
+        # past the select-only size: the attention selects in its prologue
+        return synth.get("lightning_small").with_(name=name, n=20000, k=2048,
+                                                  seq_lens=(20000, 17001, 300))
+    return synth.get(name)
+
+
+@pytest.mark.parametrize("name", ["lightning_small", "lightning_fused", "block_sparse_small",
+                                  "fathom_small"])
 def test_graph_replays_match_eager(name):
-    w = synth.get(name)
+    w = _graph_workload(name)
     print(f"[graph] workload={name}", flush=True)
     inp = synth.make_inputs(w, "cuda")
     r = StepRunner(inp)
