@@ -91,6 +91,8 @@ def _edges():
                 seq_lens=(40000, 23457), page=0, seed=3510),
         L.with_(name="edge_lightning_fused_k4096", B=2, n=30000, k=4096, hq=64,
                 seq_lens=(29999, 4097), page=64, seed=3511),
+        L.with_(name="edge_lightning_fused_k1", B=3, n=16385, k=1, hq=192,
+                seq_lens=(16385, 1, 12289), page=0, seed=3512),
     ]
 
 
