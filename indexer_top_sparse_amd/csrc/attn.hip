@@ -276,7 +276,9 @@ __host__ __device__ inline bool mla_shape(const sparse_attn_args& a) {
 }
 constexpr int kMlaRow = 576 + 8;                   // LDS row stride (elements)
 constexpr int kMlaChunks = kTT * 72;               // 16-byte chunks per tile
-constexpr int kMlaNch = (kMlaChunks + kMlaThreads - 1) / kMlaThreads;  // 5
+constexpr int kMlaNchS = 3, kMlaNchP = 6;          // per score / P V thread
+constexpr int kMlaNch = kMlaNchP;
+static_assert(256 * (kMlaNchS + kMlaNchP) == kMlaChunks, "the two roles copy a whole tile");
 constexpr int kMlaPad = 3 * kTT;  // row-table entries past a split (prefetch)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -388,16 +390,20 @@ __global__ __launch_bounds__(kMlaThreads, 1) void attn_mla_kernel(AttnPlan p) {
   for (int i = cnt + tid; i < (ntiles + 3) * kTT; i += kMlaThreads) rowp_s[i] = dummy;
 
   // gather coordinates: chunk i of this thread is row crow[i], byte offset
-  // coff[i] of the row; the last chunk index may fall past the tile
+  // coff[i] of the row.  A score thread copies kMlaNchS of a tile's 16-byte
+  // chunks and a P V thread kMlaNchP: the score waves set the pace of a tile
+  // step, so the P V waves take two thirds of the copying (lightning_128k
+  // level, hot_16k without misses 2735-2749 -> 2802-2835 steps/s against an
+  // even split; 1 : 8 and 2 : 7 were slower than 3 : 6)
+  const int nch = qk_wave ? kMlaNchS : kMlaNchP;
   int crow[kMlaNch], coff[kMlaNch];
 #pragma unroll
   for (int i = 0; i < kMlaNch; ++i) {
-    const int q = tid + i * kMlaThreads;
-    const int qc = q < kMlaChunks ? q : kMlaChunks - 1;
+    const int q = qk_wave ? tid + 256 * i : 256 * kMlaNchS + (tid - 256) + 256 * i;
+    const int qc = i < nch ? q : 0;
     crow[i] = qc / 72;
     coff[i] = 16 * (qc % 72);
   }
-  const bool last_chunk = tid + (kMlaNch - 1) * kMlaThreads < kMlaChunks;
 
   // Row gathers are non-temporal: the rows are read once per head group,
   // and the two head groups of a split share them through L2 all the same
@@ -405,13 +411,14 @@ __global__ __launch_bounds__(kMlaThreads, 1) void attn_mla_kernel(AttnPlan p) {
   auto gather = [&](u32x4 (&pre)[kMlaNch], int tile) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < kMlaNch; ++i)
-      pre[i] = __builtin_nontemporal_load(
-          (gptr<const u32x4>)((const char*)rowp_s[tile * kTT + crow[i]] + coff[i]));
+      if (i < nch)
+        pre[i] = __builtin_nontemporal_load(
+            (gptr<const u32x4>)((const char*)rowp_s[tile * kTT + crow[i]] + coff[i]));
   };
   auto commit = [&](const u32x4 (&pre)[kMlaNch], int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < kMlaNch; ++i)
-      if (i < kMlaNch - 1 || last_chunk)
+      if (i < nch)
         *(u32x4*)(&ks_s[buf][crow[i] * kMlaRow + (coff[i] >> 1)]) = pre[i];
   };
   // the first three tiles: two in LDS, one in registers
