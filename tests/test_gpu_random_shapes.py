@@ -1,7 +1,7 @@
 """GPU: whole decode steps at seeded random shapes of every score kind,
 against the oracle.
 
-Sixteen shapes are drawn once from a fixed seed around the small workloads:
+Twenty shapes are drawn once from fixed seeds around the small workloads:
 batch 1..4, context lengths that end mid-tile, valid lengths down to a
 single token, k from 1 up to more than a request's valid units, 32 or 64
 index heads, 64..256 latent attention heads, paged and contiguous latent
@@ -60,6 +60,18 @@ def _shapes():
             name=f"rand_fathom_{i}", B=B, n=n, seq_lens=seq,
             k=int(g.choice([1, 100, 300, 2048])), budget=int(g.choice([8, 92, 300, 512])),
             seed=3400 + i))
+    # latent rows long enough that the attention selects from the fused
+    # filter's candidates (a separate generator, so the shapes above stay)
+    g2 = np.random.default_rng(20261204)
+    for i in range(4):
+        B = int(g2.integers(1, 4))
+        n = int(g2.integers(12289, 60000))
+        seq = tuple(int(x) for x in g2.integers(1, n + 1, size=B))
+        out.append(synth.get("lightning_small").with_(
+            name=f"rand_lightning_fused_{i}", B=B, n=n, seq_lens=seq,
+            k=int(g2.choice([64, 300, 2048, 3000])), idx_heads=int(g2.choice([32, 64])),
+            hq=int(g2.choice([64, 128, 256])), page=int(g2.choice([0, 64])),
+            seed=3600 + i))
     return out
 
 
