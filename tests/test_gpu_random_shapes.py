@@ -78,7 +78,7 @@ def _shapes():
 def _edges():
     """Boundary shapes: one tile plus one token, a span plus one, k at or above
     the valid units, a single block or word, rows just past the select-only
-    size."""
+    size, requests with no valid token."""
     L = synth.get("lightning_small")
     Bk = synth.get("block_sparse_small")
     T = synth.get("tiny_fp32_small")
@@ -105,6 +105,15 @@ def _edges():
                 seq_lens=(29999, 4097), page=64, seed=3511),
         L.with_(name="edge_lightning_fused_k1", B=3, n=16385, k=1, hq=192,
                 seq_lens=(16385, 1, 12289), page=0, seed=3512),
+        # a request with no valid token: an all -1 selection, output 0,
+        # log-sum-exp -inf (every kind; latent rows on both select paths)
+        L.with_(name="edge_empty_lightning", B=2, n=500, k=64, seq_lens=(0, 500), page=64,
+                seed=3513),
+        L.with_(name="edge_empty_lightning_fused", B=2, n=13000, k=512, seq_lens=(13000, 0),
+                page=64, seed=3514),
+        Bk.with_(name="edge_empty_block", B=2, n=700, k=4, seq_lens=(0, 700), seed=3515),
+        T.with_(name="edge_empty_dot", B=2, n=600, k=17, seq_lens=(600, 0), seed=3516),
+        F.with_(name="edge_empty_fathom", B=2, n=3000, k=100, seq_lens=(0, 3000), seed=3517),
     ]
 
 
