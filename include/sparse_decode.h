@@ -139,7 +139,11 @@ typedef struct sparse_index_args {
 /* Arguments of the sparse attention. */
 typedef struct sparse_attn_args {
   int32_t batch;           /* B (equal to the index pass's B in the fused step) */
-  int32_t n;               /* token capacity per request                    */
+  int32_t n;               /* token capacity per request; with n == 0 no row
+                              is ever read: k_cache, page_table and the
+                              hot-buffer pointers may be NULL (v_cache still
+                              tells K/V rows from latent rows), and every
+                              output row is 0 with log-sum-exp -inf         */
   const int32_t* seq_lens; /* [B] valid tokens; NULL = n                    */
   int32_t n_q_heads;       /* Hq                                            */
   int32_t n_kv_heads;      /* Hkv, Hq % Hkv == 0                            */

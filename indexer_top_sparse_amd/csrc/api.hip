@@ -243,6 +243,9 @@ int check_attn(const sparse_attn_args* a, int sel_heads, int k, int sel_unit) {
   const int64_t e = esize(a->dtype);
   CHECK((a->q_stride_h * e) % 16 == 0 && (a->q_stride_b * e) % 16 == 0, SPARSE_EINVAL,
         "q strides must be multiples of 16 bytes");
+  // an empty context: every selected position resolves to no token, so no
+  // KV row is read and those pointers may be NULL
+  if (a->n == 0) return SPARSE_OK;
   if (a->hot_slot) {
     CHECK(a->v_cache == nullptr && a->page_table == nullptr, SPARSE_EUNSUPPORTED,
           "hot buffer: latent contiguous rows only");
