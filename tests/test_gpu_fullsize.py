@@ -120,6 +120,25 @@ def test_lightning_long_spans_ragged():
     _rerun_identical(r)
 
 
+def test_lightning_max_context():
+    """One request at the largest context the boundary accepts (4194304
+    tokens, 4.8 GB of paged latent rows): 512 histogram parts per row, so the
+    top-k takes the bin, chunk-filter and select kernels."""
+    n = 1 << 22
+    w = synth.get("lightning_128k").with_(name="lightning_4m", B=1, n=n, seq_lens=(n - 5,),
+                                          seed=1014)
+    print(f"[full] {w.name} n={n}", flush=True)
+    inp = synth.make_inputs(w, "cuda")
+    r = StepRunner(inp)
+    r.run()
+    torch.cuda.synchronize()
+    gsel = r.topk.cpu().numpy()
+    _check_rows(gsel, w)
+    scores = r.index_scores().cpu().numpy()
+    _check_lightning_sample(w, inp, r, scores, gsel, (0,))
+    _rerun_identical(r)
+
+
 def test_block_sparse_80k_full():
     w = synth.get("block_sparse_80k")
     print(f"[full] {w.name}", flush=True)
