@@ -114,6 +114,9 @@ def _edges():
         Bk.with_(name="edge_empty_block", B=2, n=700, k=4, seq_lens=(0, 700), seed=3515),
         T.with_(name="edge_empty_dot", B=2, n=600, k=17, seq_lens=(600, 0), seed=3516),
         F.with_(name="edge_empty_fathom", B=2, n=3000, k=100, seq_lens=(0, 3000), seed=3517),
+        # a zero bit budget: no plane is read, every score is the constant
+        F.with_(name="edge_fathom_budget0", B=1, n=5000, k=100, budget=0, seq_lens=(4999,),
+                seed=3518),
     ]
 
 
