@@ -259,10 +259,12 @@ constexpr int kMaxSplitTok = 2048;  // row-table entries of one split
 // The token order of the P V contraction is permuted so that the eight
 // probabilities a score lane holds (tokens 4g..4g+3 and 16+4g..16+4g+3,
 // g = lane / 16) are exactly one lane's B operand.  K tiles rotate through
-// three LDS buffers with one more tile in flight in registers; the score
-// waves run one tile ahead of the P V waves.  Probabilities are taken
+// three LDS buffers with one more tile in flight in registers, copied by
+// all eight waves (a P V thread twice the chunks of a score thread); the
+// score waves run one tile ahead of the P V waves.  Probabilities are taken
 // relative to a per-head reference max that moves (rescaling O and the
-// sum) only when a tile's max exceeds it by more than 2^8.
+// sum) only when a tile's max exceeds it by more than 2^8.  In the fused
+// step the kernel first makes the request's top-k selection itself (FSEL).
 constexpr int kMlaWaves = 8;
 constexpr int kMlaHeadsWG = 64;
 constexpr int kMlaThreads = 64 * kMlaWaves;
